@@ -1,0 +1,85 @@
+"""Single-query paged decode attention over TQ pages (dequantise, then softmax).
+
+Test infrastructure (see ``oracle/__init__.py``).
+
+Sources: "Architecture", "Diagnostic vs Serving Paths" (the TQ paged decode
+reference reads packed pages and reconstructs rows inside the loop) and
+"Cache Storage Objects" (page shape); "vLLM Usage", "TQ Packed Page
+Contract" (``decode_tq4_paged``) and "Live Backend Gap" (decode through
+block tables).
+
+This is the plain definition, with no rotated-domain algebra: every key and
+value row of the sequence is reconstructed densely in float64
+(``k_t = n_k irht(c_K[idx_K])``), scores are ``scale <q, k_t>``, the softmax
+subtracts the maximum, and the output is ``sum_t p_t v_t``.
+
+Readings taken: query head h uses KV head ``h // (Hq / Hkv)``; the default
+scale is ``1 / sqrt(head_dim)``; token t of sequence b lives in page
+``block_table[b, t // block_size]`` at offset ``t % block_size``; a sequence
+of length 0 produces zeros; rows that were never written decode to whatever
+bytes the page holds (all-zero bytes decode to the zero vector).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codec import dequantize_rows
+
+__all__ = ["gather_rows", "paged_decode", "paged_decode_heads"]
+
+
+def gather_rows(pages, block_table_row, length, kv_head):
+    """Row bytes of tokens 0..length-1 of one sequence for one KV head."""
+    BS = pages.shape[1]
+    t = np.arange(length)
+    blocks = np.asarray(block_table_row)[t // BS]
+    return pages[blocks, t % BS, kv_head]
+
+
+def _attend(q64, K, V, scale):
+    s = scale * (K @ q64)
+    s = s - s.max()
+    p = np.exp(s)
+    p /= p.sum()
+    return p @ V
+
+
+def paged_decode_heads(q, k_pages, v_pages, block_table, seq_lens, k_bits, v_bits,
+                       signs, ck32, cv32, heads, scale=None):
+    """Outputs for the listed ``(b, h)`` pairs only -> float64 [len(heads), d].
+
+    Reconstructs just the rows those heads need (used to check large
+    workloads on a sample of heads).
+    """
+    q = np.asarray(q)
+    B, Hq, d = q.shape
+    Hkv = k_pages.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    out = np.zeros((len(heads), d), dtype=np.float64)
+    cache = {}
+    for i, (b, h) in enumerate(heads):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        g = h // G
+        key = (b, g)
+        if key not in cache:
+            K = dequantize_rows(gather_rows(k_pages, block_table[b], L, g), k_bits, d, signs, ck32)
+            V = dequantize_rows(gather_rows(v_pages, block_table[b], L, g), v_bits, d, signs, cv32)
+            cache = {key: (K, V)}
+        K, V = cache[key]
+        out[i] = _attend(q[b, h].astype(np.float64), K, V, scale)
+    return out
+
+
+def paged_decode(q, k_pages, v_pages, block_table, seq_lens, k_bits, v_bits,
+                 signs, ck32, cv32, scale=None):
+    """Full decode: float32 ``[B, Hq, d]`` (computed in float64, rounded once)."""
+    q = np.asarray(q)
+    B, Hq, d = q.shape
+    heads = [(b, h) for b in range(B) for h in range(Hq)]
+    out = paged_decode_heads(q, k_pages, v_pages, block_table, seq_lens, k_bits, v_bits,
+                             signs, ck32, cv32, heads, scale)
+    return out.reshape(B, Hq, d).astype(np.float32)
