@@ -1,0 +1,161 @@
+/*
+ * tq.h -- C ABI of the TurboQuant packed-page KV library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library writes K/V rows into uint8 pages in the TQ row format and runs
+ * single-query paged decode attention over those pages.  Everything below is
+ * plain C: device buffers are raw device pointers, streams are hipStream_t
+ * passed as void*.  The library never allocates device memory inside
+ * tq_write_kv / tq_paged_decode and never synchronises the stream; the caller
+ * owns every buffer.
+ *
+ * Definitions this ABI implements (TurboQuant documentation pages):
+ *
+ *  - Row format ("vLLM Usage", section "TQ Byte Layout"): for one component
+ *    (K or V), one token and one KV head, a row is
+ *    index_bytes = ceil(head_dim * bits / 8) bytes of bit-packed codebook
+ *    indices followed by the 4-byte fp32 norm of the raw row
+ *    (row_bytes = index_bytes + 4; 36/52/68/84 bytes for 2/3/4/5 bits at
+ *    head_dim 128).  K and V are stored independently with their own bits.
+ *    Indices form one LSB-first bit stream: index i occupies stream bits
+ *    [i*bits, (i+1)*bits), stream bit 8j+k is bit k of byte j.  The norm is
+ *    little-endian.  No row or page padding.
+ *  - Page tensor ("Architecture", section "Cache Storage Objects"):
+ *    uint8 [num_blocks, block_size, num_kv_heads, row_bytes], one tensor per
+ *    component, contiguous.
+ *  - Flat slots ("vLLM Usage", section "Slot Mapping"): token n goes to page
+ *    slot / block_size at offset slot % block_size; negative slots are
+ *    ignored; a slot beyond the allocated pages is an error.
+ *  - Codec ("vLLM Usage", "TQ Packed Page Contract"; "vLLM Reference Audit",
+ *    Feature Checklist): a row x is encoded as n = ||x||_2 (float64 sum of
+ *    squares, rounded once to fp32), u = x / n, r = H (s * u) / sqrt(d)
+ *    (randomized Hadamard transform: seeded +-1 signs s, then the orthonormal
+ *    Sylvester Hadamard matrix), and each r_i is replaced by the index of its
+ *    nearest centroid of the 2^bits-level Lloyd-Max codebook of the exact
+ *    coordinate law of a uniform unit vector in R^d.  The signs come from
+ *    SplitMix64 seeded with the rotation seed (s_i = -1 when bit 63 of the
+ *    i-th output is set).
+ *  - Decode ("Architecture", section "Diagnostic vs Serving Paths"; "vLLM
+ *    Usage", "Live Backend Gap"): one query token per sequence; query head h
+ *    attends to KV head h / (num_q_heads / num_kv_heads) over tokens
+ *    0..seq_lens[b]-1 found through block_table[b, t / block_size];
+ *    out = softmax(scale * q . k_t) . v_t with k_t, v_t the reconstructed rows
+ *    n * R^T c[idx].  A sequence of length 0 yields zeros.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1,  /* null pointer, bad size, inconsistent shapes */
+  TQ_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement */
+  TQ_ERR_ALIGNMENT = 3,    /* a pointer is not aligned as documented */
+  TQ_ERR_WORKSPACE = 4,    /* workspace smaller than tq_decode_workspace_bytes */
+  TQ_ERR_HIP = 5,          /* a HIP runtime call failed (see tq_last_hip_error) */
+  TQ_ERR_NO_DEVICE = 6     /* no gfx950 device is current */
+} tq_status;
+
+typedef enum tq_dtype {
+  TQ_F32 = 0,
+  TQ_F16 = 1,
+  TQ_BF16 = 2
+} tq_dtype;
+
+/* Opaque, immutable after creation; host memory only (no device state), so
+ * one context may serve every device and concurrent calls. */
+typedef struct tq_ctx tq_ctx;
+
+/* Human-readable name of a status code (static string). */
+const char* tq_status_string(tq_status status);
+
+/* Last HIP error code seen by this thread (0 if none). */
+int tq_last_hip_error(void);
+
+/* Row size in bytes: ceil(head_dim * bits / 8) + 4.  Returns 0 when
+ * head_dim <= 0 or bits is outside 1..8 ("vLLM Usage", "TQ Byte Layout"). */
+size_t tq_row_bytes(int head_dim, int bits);
+
+/* Host-only: the 2^bits fp32 centroids (increasing) and 2^bits - 1 fp32
+ * boundaries (midpoints of neighbouring centroids, rounded to fp32) of the
+ * Lloyd-Max codebook of the coordinate law f(x) ~ (1 - x^2)^((d-3)/2) on
+ * [-1, 1] ("vLLM Reference Audit", File Map row "Lloyd-Max codebooks":
+ * centroids and boundaries; Feature Checklist: exact Beta law).
+ * centroids: 2^bits floats; boundaries: 2^bits - 1 floats or NULL.
+ * head_dim in 3..4096, bits in 1..5.  Deterministic. */
+tq_status tq_codebook(int head_dim, int bits, float* centroids, float* boundaries);
+
+/* Host-only: the head_dim rotation signs (+1/-1) for a seed ("vLLM Usage",
+ * "TQ Packed Page Contract": RHT rotation built from a seed). */
+tq_status tq_rht_signs(uint64_t seed, int head_dim, int8_t* signs);
+
+/* Create a context for one head dimension and rotation seed: computes the
+ * signs and the codebooks for bits 1..5 on the host.  head_dim must be 128
+ * (the only width the kernels are built for).  Does not touch the GPU. */
+tq_status tq_ctx_create(int head_dim, uint64_t rht_seed, tq_ctx** out);
+tq_status tq_ctx_destroy(tq_ctx* ctx);
+
+/* Write rows into pages ("vLLM Usage", "Slot Mapping" and "TQ Packed Page
+ * Contract", write_tq4_kv).
+ *   raw       device, [num_tokens, num_kv_heads, head_dim] of raw_dtype,
+ *             contiguous, 4-byte aligned (16-byte aligned for best speed).
+ *   pages     device, uint8 [num_blocks, block_size, num_kv_heads,
+ *             tq_row_bytes(head_dim, bits)], contiguous, 4-byte aligned.
+ *   slots     device, int64 [num_tokens].  slot < 0: token skipped, pages
+ *             untouched.  slot >= num_blocks * block_size: token skipped and
+ *             counted in *err_count.
+ *   bits      2..5.
+ *   err_count device int32 or NULL; the kernel atomically ADDS the number of
+ *             out-of-range slots (the caller zeroes it beforehand).
+ *   stream    hipStream_t (NULL = default stream).
+ * Asynchronous; the caller keeps every buffer alive until the stream has
+ * executed the call.  Two tokens mapping to the same slot race (undefined
+ * which one lands). */
+tq_status tq_write_kv(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype,
+                      int64_t num_tokens, int num_kv_heads, uint8_t* pages,
+                      int64_t num_blocks, int block_size, const int64_t* slots,
+                      int bits, int32_t* err_count, void* stream);
+
+/* Bytes of device workspace tq_paged_decode needs for these sizes. */
+size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
+                                 int num_kv_heads, int max_seq_len, int block_size);
+
+/* Single-query paged decode attention over TQ pages ("Architecture",
+ * "Diagnostic vs Serving Paths": the paged decode reads packed pages and
+ * reconstructs rows inside the loop; "vLLM Usage", decode_tq4_paged).
+ *   q            device, [batch, num_q_heads, head_dim] of q_dtype, contiguous.
+ *   k_pages      device, uint8 [num_blocks, block_size, num_kv_heads,
+ *                tq_row_bytes(head_dim, k_bits)], 16-byte aligned.
+ *   v_pages      same with v_bits.
+ *   block_table  device, int32 [batch, max_blocks_per_seq]; entries for pages
+ *                beyond a sequence's length are never read.
+ *   seq_lens     device, int32 [batch], each in 0..max_seq_len.
+ *   max_seq_len  host upper bound of seq_lens (sizes the work split).
+ *   scale        softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *   out          device, fp32 [batch, num_q_heads, head_dim].
+ *   workspace    device, >= tq_decode_workspace_bytes(...) bytes, 16-byte
+ *                aligned; contents are scratch.
+ * Supported: head_dim 128, block_size 16, k_bits/v_bits 2..5,
+ * num_q_heads / num_kv_heads in 1..16.  Asynchronous; block ids and lengths
+ * are trusted (an out-of-range block id reads out of bounds). */
+tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype,
+                          int batch, int num_q_heads, int num_kv_heads,
+                          const uint8_t* k_pages, int k_bits,
+                          const uint8_t* v_pages, int v_bits,
+                          int64_t num_blocks, int block_size,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* seq_lens, int max_seq_len, float scale,
+                          float* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

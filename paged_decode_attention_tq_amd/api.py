@@ -1,0 +1,153 @@
+"""Python entry points over the C ABI (same names as include/tq.h).
+
+PyTorch supplies device memory and the current HIP stream; every step of
+the write and the decode runs in the HIP kernels of ``libtq.so``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import TQError, check
+
+__all__ = [
+    "TQError",
+    "row_bytes",
+    "codebook",
+    "rht_signs",
+    "Context",
+    "write_kv",
+    "decode_workspace_bytes",
+    "paged_decode",
+]
+
+_DTYPES = {torch.float32: _lib.TQ_F32, torch.float16: _lib.TQ_F16, torch.bfloat16: _lib.TQ_BF16}
+
+
+def row_bytes(head_dim: int, bits: int) -> int:
+    return int(_lib.lib().tq_row_bytes(head_dim, bits))
+
+
+def codebook(head_dim: int, bits: int):
+    """(centroids[2^b], boundaries[2^b - 1]) as float32 numpy arrays (host solver)."""
+    n = 1 << bits
+    c = np.zeros(n, np.float32)
+    t = np.zeros(n - 1, np.float32)
+    check(_lib.lib().tq_codebook(head_dim, bits, c.ctypes.data, t.ctypes.data), "tq_codebook")
+    return c, t
+
+
+def rht_signs(seed: int, head_dim: int) -> np.ndarray:
+    s = np.zeros(head_dim, np.int8)
+    check(_lib.lib().tq_rht_signs(seed, head_dim, s.ctypes.data), "tq_rht_signs")
+    return s
+
+
+class Context:
+    """Rotation signs and codebooks for one head_dim and seed (host memory only)."""
+
+    def __init__(self, head_dim: int = 128, seed: int = 42):
+        self.head_dim = int(head_dim)
+        self.seed = int(seed)
+        h = ctypes.c_void_p()
+        check(_lib.lib().tq_ctx_create(self.head_dim, self.seed, ctypes.byref(h)), "tq_ctx_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                _lib.lib().tq_ctx_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def write_kv(ctx: Context, raw: torch.Tensor, pages: torch.Tensor, slots: torch.Tensor, bits: int,
+             err_count: torch.Tensor | None = None, check_slots: bool = True) -> int:
+    """Encode ``raw[N, Hkv, d]`` into ``pages[NB, BS, Hkv, RB]`` at ``slots[N]``.
+
+    Negative slots are skipped.  Out-of-range slots are skipped and counted;
+    with ``check_slots`` the call synchronises and raises ``TQError`` if any
+    were found.  Returns the number of out-of-range slots when checked.
+    """
+    _need(raw.is_cuda and pages.is_cuda and slots.is_cuda, "tensors must be on the GPU")
+    _need(raw.dim() == 3 and raw.shape[2] == ctx.head_dim and raw.is_contiguous(), "raw must be [N, Hkv, d]")
+    _need(pages.dtype == torch.uint8 and pages.dim() == 4 and pages.is_contiguous(), "pages must be uint8 4-D")
+    NB, BS, Hkv, RB = pages.shape
+    _need(raw.shape[1] == Hkv, "num_kv_heads mismatch")
+    _need(RB == row_bytes(ctx.head_dim, bits), "pages row_bytes does not match bits")
+    _need(slots.dtype == torch.int64 and slots.shape == (raw.shape[0],) and slots.is_contiguous(),
+          "slots must be int64 [N]")
+    _need(raw.dtype in _DTYPES, "raw dtype must be fp32/fp16/bf16")
+    own = err_count is None and check_slots
+    if own:
+        err_count = torch.zeros(1, dtype=torch.int32, device=raw.device)
+    st = _lib.lib().tq_write_kv(
+        ctx.handle, raw.data_ptr(), _DTYPES[raw.dtype], raw.shape[0], Hkv, pages.data_ptr(), NB, BS,
+        slots.data_ptr(), bits, err_count.data_ptr() if err_count is not None else None, _stream(raw))
+    check(st, "tq_write_kv")
+    if check_slots:
+        n_bad = int(err_count.item())
+        if n_bad:
+            raise TQError(f"tq_write_kv: {n_bad} slot(s) outside the allocated pages")
+        return n_bad
+    return 0
+
+
+def decode_workspace_bytes(ctx: Context, batch, num_q_heads, num_kv_heads, max_seq_len, block_size=16) -> int:
+    return int(_lib.lib().tq_decode_workspace_bytes(ctx.handle, batch, num_q_heads, num_kv_heads,
+                                                    max_seq_len, block_size))
+
+
+def paged_decode(ctx: Context, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                 block_table: torch.Tensor, seq_lens: torch.Tensor, k_bits: int, v_bits: int,
+                 max_seq_len: int | None = None, scale: float | None = None,
+                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Single-query paged decode -> fp32 ``[B, Hq, d]``.
+
+    ``max_seq_len`` defaults to ``seq_lens.max()`` (a device-to-host sync).
+    """
+    _need(q.is_cuda and q.dim() == 3 and q.shape[2] == ctx.head_dim and q.is_contiguous(), "q must be [B, Hq, d]")
+    _need(q.dtype in _DTYPES, "q dtype must be fp32/fp16/bf16")
+    B, Hq, d = q.shape
+    for name, pg, bits in (("k_pages", k_pages, k_bits), ("v_pages", v_pages, v_bits)):
+        _need(pg.dtype == torch.uint8 and pg.dim() == 4 and pg.is_contiguous(), f"{name} must be uint8 4-D")
+        _need(pg.shape[3] == row_bytes(d, bits), f"{name} row_bytes does not match bits")
+    NB, BS, Hkv, _ = k_pages.shape
+    _need(tuple(v_pages.shape[:3]) == (NB, BS, Hkv), "k_pages / v_pages geometry mismatch")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B
+          and block_table.is_contiguous(), "block_table must be int32 [B, max_blocks]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (B,), "seq_lens must be int32 [B]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out.dtype == torch.float32 and out.shape == (B, Hq, d) and out.is_contiguous(), "out must be fp32 [B, Hq, d]")
+    need = decode_workspace_bytes(ctx, B, Hq, Hkv, max_seq_len, BS)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = _lib.lib().tq_paged_decode(
+        ctx.handle, q.data_ptr(), _DTYPES[q.dtype], B, Hq, Hkv, k_pages.data_ptr(), k_bits,
+        v_pages.data_ptr(), v_bits, NB, BS, block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), max_seq_len, float(scale) if scale else 0.0, out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
+    check(st, "tq_paged_decode")
+    return out

@@ -1,0 +1,424 @@
+// Host side of the TurboQuant packed-page KV library: the C ABI declared in
+// include/tq.h, argument validation, the context (rotation signs and
+// Lloyd-Max codebooks computed on the host), and work-split selection for
+// the decode kernels.
+//
+// Sources: TurboQuant documentation pages "vLLM Usage" (sections "TQ Byte
+// Layout", "Slot Mapping", "TQ Packed Page Contract"), "vLLM Reference
+// Audit" (Feature Checklist: Lloyd-Max codebooks with the exact Beta law,
+// RHT transforms, 1..5-bit packing) and "Architecture" ("Cache Storage
+// Objects", "Diagnostic vs Serving Paths").
+
+#include "tq.h"
+#include "tq_internal.h"
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <new>
+
+using tq::kHeadDim;
+
+struct tq_ctx {
+  int head_dim;
+  uint64_t seed;
+  int8_t signs[kHeadDim];
+  uint32_t sign_bits[kHeadDim / 32];
+  float cent[6][32];     // [bits][j], bits 1..5
+  float bound[6][31];
+  float v_scale[6];      // fp16-friendly scale of the value centroids per bits
+};
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+tq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return TQ_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return TQ_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): the rotation's sign source.
+uint64_t splitmix64_next(uint64_t& state) {
+  state += 0x9E3779B97F4A7C15ull;
+  uint64_t z = state;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// ---------------------------------------------------------------------------
+// Lloyd-Max codebook of the coordinate law of a uniform unit vector in R^d:
+// f(x) = K (1 - x^2)^m on [-1, 1], m = (d - 3) / 2, in long double.
+//
+// Cell masses use the antiderivative J_m(x) = int_0^x (1 - t^2)^m dt from the
+// recursion (2m + 1) J_m = x (1 - x^2)^m + 2m J_{m-1}, started at
+// J_0 = x (integer m) or J_{-1/2} = asin(x) (half-integer m).  First moments
+// are closed form: int x (1 - x^2)^m = -(1 - x^2)^(m+1) / (2(m + 1)).
+class CoordinateLaw {
+ public:
+  explicit CoordinateLaw(int d) : d_(d), m_((d - 3) / 2.0L) {
+    logK_ = lgammal(d / 2.0L) - 0.5L * logl(3.14159265358979323846264338327950288L) -
+            lgammal((d - 1) / 2.0L);
+    half_integer_ = (d % 2) == 0;  // m = (d-3)/2 is half-integer for even d
+  }
+
+  long double J(long double x) const {
+    long double w = 1.0L - x * x;
+    if (w < 0) w = 0;
+    long double mm, val, pw;
+    if (half_integer_) {
+      mm = -0.5L;
+      val = asinl(x);
+      pw = sqrtl(w);  // w^(mm + 1)
+    } else {
+      mm = 0.0L;
+      val = x;
+      pw = w;
+    }
+    while (mm < m_ - 0.25L) {
+      mm += 1.0L;
+      val = (x * pw + 2.0L * mm * val) / (2.0L * mm + 1.0L);
+      pw *= w;
+    }
+    return val;
+  }
+
+  long double K() const { return expl(logK_); }
+  long double W(long double x) const {  // (1 - x^2)^(m + 1)
+    long double w = 1.0L - x * x;
+    return w <= 0 ? 0.0L : powl(w, m_ + 1);
+  }
+  long double m() const { return m_; }
+
+  long double mass(long double a, long double b) const { return expl(logK_) * (J(b) - J(a)); }
+
+  long double moment(long double a, long double b) const {
+    long double wa = 1.0L - a * a, wb = 1.0L - b * b;
+    if (wa < 0) wa = 0;
+    if (wb < 0) wb = 0;
+    return expl(logK_) * (powl(wa, m_ + 1) - powl(wb, m_ + 1)) / (2.0L * (m_ + 1));
+  }
+
+ private:
+  int d_;
+  long double m_;
+  long double logK_;
+  bool half_integer_;
+};
+
+void solve_codebook(int d, int bits, float* cent32, float* bound32) {
+  const int n = 1 << bits;
+  CoordinateLaw law(d);
+  long double c[32], cn[32], e[33];
+  // start: evenly spaced over +-3 standard deviations of the law (1/sqrt(d))
+  const long double spread = fminl(0.95L, 3.0L / sqrtl((long double)d));
+  for (int j = 0; j < n; ++j) c[j] = spread * ((2.0L * j + 1) / n - 1.0L);
+  long double Jv[33], Wv[33];
+  const long double K = law.K();
+  int tail = -1;  // iterations left once the steps reach the rounding noise
+  for (int it = 0; it < 100000; ++it) {
+    e[0] = -1.0L;
+    e[n] = 1.0L;
+    for (int j = 1; j < n; ++j) e[j] = 0.5L * (c[j - 1] + c[j]);
+    for (int k = 0; k <= n; ++k) {
+      Jv[k] = law.J(e[k]);
+      Wv[k] = law.W(e[k]);
+    }
+    long double step = 0;
+    for (int j = 0; j < n; ++j) {
+      const long double mass = K * (Jv[j + 1] - Jv[j]);
+      const long double mom = K * (Wv[j] - Wv[j + 1]) / (2.0L * (law.m() + 1));
+      cn[j] = mom / mass;
+      step = fmaxl(step, fabsl(cn[j] - c[j]));
+    }
+    for (int j = 0; j < n; ++j) c[j] = cn[j];
+    if (step < 1e-18L) break;
+    // long double rounding noise keeps the steps near 1e-17..1e-16; run a
+    // few hundred more iterations once below 1e-16, then stop
+    if (tail < 0 && step < 1e-16L) tail = 400;
+    if (tail >= 0 && tail-- == 0) break;
+  }
+  for (int j = 0; j < n; ++j) cent32[j] = (float)(0.5L * (c[j] - c[n - 1 - j]));
+  if (bound32)
+    for (int j = 0; j + 1 < n; ++j)
+      bound32[j] = (float)(0.5 * ((double)cent32[j] + (double)cent32[j + 1]));
+}
+
+// fp32 -> fp16 bits, round to nearest even (normal and subnormal range).
+uint16_t f32_to_f16_bits(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  uint32_t sign = (x >> 16) & 0x8000u;
+  uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax >= 0x47800000u) return (uint16_t)(sign | (ax > 0x7F800000u ? 0x7E00u : 0x7C00u));
+  if (ax < 0x33000000u) return (uint16_t)sign;  // below half the smallest subnormal
+  int exp = (int)(ax >> 23) - 127;
+  uint32_t mant = (ax & 0x7FFFFFu) | 0x800000u;
+  int shift = (exp < -14) ? (13 + (-14 - exp)) : 13;
+  uint32_t r = mant >> shift;
+  uint32_t rem = mant & ((1u << shift) - 1);
+  uint32_t halfway = 1u << (shift - 1);
+  if (rem > halfway || (rem == halfway && (r & 1))) ++r;
+  uint32_t out = (exp < -14) ? r : ((uint32_t)(exp + 15) << 10) + (r - 0x400u);
+  return (uint16_t)(sign | out);
+}
+
+float f16_bits_to_f32(uint16_t h) {
+  uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  uint32_t e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  float v;
+  if (e == 0)
+    v = std::ldexp((float)m, -24);
+  else
+    v = std::ldexp((float)(m | 0x400), (int)e - 25);
+  uint32_t bitsv;
+  std::memcpy(&bitsv, &v, 4);
+  bitsv |= sign;
+  std::memcpy(&v, &bitsv, 4);
+  return v;
+}
+
+// Scale s in [1, 2) for which the fp16 roundings of s*c_j have the smallest
+// worst relative error; the value tables of the decode hold fp16(s * c_j)
+// and the output is divided by s at the end.
+float best_fp16_scale(const float* c, int n) {
+  float best_s = 1.0f;
+  double best_err = 1e30;
+  for (int k = 0; k < (1 << 18); ++k) {
+    float s = 1.0f + (float)k / (float)(1 << 18);
+    double worst = 0;
+    for (int j = n / 2; j < n; ++j) {  // magnitudes (the codebook is symmetric)
+      float v = s * c[j];
+      double err = std::fabs((double)f16_bits_to_f32(f32_to_f16_bits(v)) - (double)v) / (double)v;
+      if (err > worst) worst = err;
+      if (worst >= best_err) break;
+    }
+    if (worst < best_err) {
+      best_err = worst;
+      best_s = s;
+    }
+  }
+  return best_s;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+// Decode work split: every (sequence, KV head) is cut into splits of
+// pages_per_split pages, one wave each.
+struct SplitPlan {
+  int pages_per_split;
+  int num_splits;
+};
+
+SplitPlan plan_split(int batch, int num_kv_heads, int max_seq_len, int num_cus) {
+  const int max_pages = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
+  SplitPlan p;
+  if (max_pages <= 0) {
+    p.pages_per_split = 1;
+    p.num_splits = 1;
+    return p;
+  }
+  const long long work = (long long)batch * num_kv_heads * max_pages;
+  const long long target_waves = (long long)num_cus * 32;
+  long long pps = (work + target_waves - 1) / target_waves;
+  if (pps < 16) pps = 16;
+  if (pps > max_pages) pps = max_pages;
+  p.pages_per_split = (int)pps;
+  p.num_splits = (int)((max_pages + pps - 1) / pps);
+  return p;
+}
+
+bool bits_ok(int b) { return b >= 2 && b <= 5; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TQ_ERR_ALIGNMENT: return "misaligned pointer";
+    case TQ_ERR_WORKSPACE: return "workspace too small";
+    case TQ_ERR_HIP: return "HIP runtime error";
+    case TQ_ERR_NO_DEVICE: return "no gfx950 device";
+  }
+  return "unknown status";
+}
+
+int tq_last_hip_error(void) { return g_last_hip_error; }
+
+size_t tq_row_bytes(int head_dim, int bits) {
+  if (head_dim <= 0 || bits < 1 || bits > 8) return 0;
+  return ((size_t)head_dim * bits + 7) / 8 + 4;
+}
+
+tq_status tq_codebook(int head_dim, int bits, float* centroids, float* boundaries) {
+  if (!centroids || head_dim < 3 || head_dim > 4096 || bits < 1 || bits > 5) return TQ_ERR_INVALID_ARG;
+  solve_codebook(head_dim, bits, centroids, boundaries);
+  return TQ_OK;
+}
+
+tq_status tq_rht_signs(uint64_t seed, int head_dim, int8_t* signs) {
+  if (!signs || head_dim <= 0) return TQ_ERR_INVALID_ARG;
+  uint64_t st = seed;
+  for (int i = 0; i < head_dim; ++i) signs[i] = (splitmix64_next(st) >> 63) ? -1 : 1;
+  return TQ_OK;
+}
+
+tq_status tq_ctx_create(int head_dim, uint64_t rht_seed, tq_ctx** out) {
+  if (!out) return TQ_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (head_dim != kHeadDim) return TQ_ERR_UNSUPPORTED;
+  tq_ctx* c = new (std::nothrow) tq_ctx;
+  if (!c) return TQ_ERR_INVALID_ARG;
+  std::memset(c, 0, sizeof(*c));
+  c->head_dim = head_dim;
+  c->seed = rht_seed;
+  tq_rht_signs(rht_seed, head_dim, c->signs);
+  for (int i = 0; i < head_dim; ++i)
+    if (c->signs[i] < 0) c->sign_bits[i >> 5] |= 1u << (i & 31);
+  for (int b = 1; b <= 5; ++b) {
+    solve_codebook(head_dim, b, c->cent[b], c->bound[b]);
+    c->v_scale[b] = best_fp16_scale(c->cent[b], 1 << b);
+  }
+  *out = c;
+  return TQ_OK;
+}
+
+tq_status tq_ctx_destroy(tq_ctx* ctx) {
+  delete ctx;
+  return TQ_OK;
+}
+
+tq_status tq_write_kv(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype, int64_t num_tokens,
+                      int num_kv_heads, uint8_t* pages, int64_t num_blocks, int block_size,
+                      const int64_t* slots, int bits, int32_t* err_count, void* stream) {
+  if (!ctx || num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || block_size <= 0)
+    return TQ_ERR_INVALID_ARG;
+  if (raw_dtype != TQ_F32 && raw_dtype != TQ_F16 && raw_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!bits_ok(bits)) return TQ_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return TQ_OK;
+  if (!raw || !pages || !slots) return TQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(raw) & 3) || (reinterpret_cast<uintptr_t>(pages) & 3) ||
+      (reinterpret_cast<uintptr_t>(slots) & 7))
+    return TQ_ERR_ALIGNMENT;
+  tq::WriteArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.raw = raw;
+  a.pages = pages;
+  a.slots = slots;
+  a.err_count = err_count;
+  a.num_rows = num_tokens * num_kv_heads;
+  a.num_slots = num_blocks * block_size;
+  a.row_bytes = (int)tq_row_bytes(kHeadDim, bits);
+  a.page_bytes = (int64_t)block_size * num_kv_heads * a.row_bytes;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  std::memcpy(a.sign_bits, ctx->sign_bits, sizeof(a.sign_bits));
+  const int n = 1 << bits;
+  for (int j = 0; j < n / 2 - 1; ++j) a.pos_bounds[j] = ctx->bound[bits][n / 2 + j];
+  return hip_status(tq::launch_write(a, (int)raw_dtype, bits, (hipStream_t)stream));
+}
+
+size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads, int num_kv_heads,
+                                 int max_seq_len, int block_size) {
+  (void)ctx;
+  (void)block_size;
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  SplitPlan p = plan_split(batch, num_kv_heads, max_seq_len, device_cu_count());
+  size_t per = (size_t)batch * num_q_heads * p.num_splits;
+  return per * (kHeadDim + 1) * sizeof(float) + 256;
+}
+
+tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
+                          int num_q_heads, int num_kv_heads, const uint8_t* k_pages, int k_bits,
+                          const uint8_t* v_pages, int v_bits, int64_t num_blocks, int block_size,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* seq_lens, int max_seq_len, float scale, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_seq_len < 0)
+    return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads) return TQ_ERR_INVALID_ARG;
+  const int group = num_q_heads / num_kv_heads;
+  if (block_size != tq::kBlockSize || group > tq::kMaxGroup || !bits_ok(k_bits) || !bits_ok(v_bits))
+    return TQ_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size < max_seq_len) return TQ_ERR_INVALID_ARG;
+  if (batch == 0) return TQ_OK;
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out) return TQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k_pages) & 15) || (reinterpret_cast<uintptr_t>(v_pages) & 15) ||
+      (reinterpret_cast<uintptr_t>(out) & 15) || (reinterpret_cast<uintptr_t>(workspace) & 15) ||
+      (reinterpret_cast<uintptr_t>(q) & 3))
+    return TQ_ERR_ALIGNMENT;
+  const size_t need =
+      tq_decode_workspace_bytes(ctx, batch, num_q_heads, num_kv_heads, max_seq_len, block_size);
+  if (!workspace || workspace_bytes < need) return TQ_ERR_WORKSPACE;
+
+  SplitPlan p = plan_split(batch, num_kv_heads, max_seq_len, device_cu_count());
+  const float sm_scale = scale > 0 ? scale : 1.0f / std::sqrt((float)kHeadDim);
+  const float v_scale = ctx->v_scale[v_bits];
+
+  tq::DecodeArgs d;
+  std::memset(&d, 0, sizeof(d));
+  d.q = q;
+  d.k_pages = k_pages;
+  d.v_pages = v_pages;
+  d.block_table = block_table;
+  d.seq_lens = seq_lens;
+  d.part_acc = static_cast<float*>(workspace);
+  d.part_lse = d.part_acc + (size_t)batch * num_q_heads * p.num_splits * kHeadDim;
+  d.k_row_bytes = (int)tq_row_bytes(kHeadDim, k_bits);
+  d.v_row_bytes = (int)tq_row_bytes(kHeadDim, v_bits);
+  d.k_page_bytes = (int64_t)block_size * num_kv_heads * d.k_row_bytes;
+  d.v_page_bytes = (int64_t)block_size * num_kv_heads * d.v_row_bytes;
+  d.batch = batch;
+  d.num_q_heads = num_q_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.group = group;
+  d.max_blocks_per_seq = max_blocks_per_seq;
+  d.pages_per_split = p.pages_per_split;
+  d.num_splits = p.num_splits;
+  d.q_scale = (float)((double)sm_scale * 1.4426950408889634 / std::sqrt((double)kHeadDim));
+  std::memcpy(d.sign_bits, ctx->sign_bits, sizeof(d.sign_bits));
+  for (int j = 0; j < (1 << k_bits); ++j) d.k_cent[j] = ctx->cent[k_bits][j];
+  for (int j = 0; j < (1 << v_bits); ++j) d.v_cent[j] = ctx->cent[v_bits][j] * v_scale;
+
+  tq_status st = hip_status(tq::launch_decode(d, (int)q_dtype, k_bits, v_bits, (hipStream_t)stream));
+  if (st != TQ_OK) return st;
+
+  tq::MergeArgs m;
+  std::memset(&m, 0, sizeof(m));
+  m.part_acc = d.part_acc;
+  m.part_lse = d.part_lse;
+  m.seq_lens = seq_lens;
+  m.out = out;
+  m.batch = batch;
+  m.num_q_heads = num_q_heads;
+  m.pages_per_split = p.pages_per_split;
+  m.num_splits = p.num_splits;
+  m.inv_v_scale_over_sqrt_d = (float)(1.0 / ((double)v_scale * std::sqrt((double)kHeadDim)));
+  std::memcpy(m.sign_bits, ctx->sign_bits, sizeof(m.sign_bits));
+  return hip_status(tq::launch_merge(m, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal structures shared by the host code (tq_host.cpp) and the HIP
+// kernels (tq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int kHeadDim = 128;    // the kernels are built for head_dim 128
+constexpr int kBlockSize = 16;   // decode page size (tokens per page)
+constexpr int kMaxGroup = 16;    // query heads per KV head handled by one wave
+
+// Arguments of the row-writer kernel (passed by value as kernel arguments).
+struct WriteArgs {
+  const void* raw;          // [num_tokens, num_kv_heads, 128]
+  uint8_t* pages;           // [num_blocks, block_size, num_kv_heads, row_bytes]
+  const int64_t* slots;     // [num_tokens]
+  int32_t* err_count;       // nullable
+  int64_t num_rows;         // num_tokens * num_kv_heads
+  int64_t num_slots;        // num_blocks * block_size
+  int64_t page_bytes;       // block_size * num_kv_heads * row_bytes
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t row_bytes;
+  uint32_t sign_bits[kHeadDim / 32];   // bit i set <=> sign_i = -1
+  float pos_bounds[16];     // the 2^(b-1) - 1 positive boundaries, increasing
+};
+
+// Arguments of the decode split kernel.
+struct DecodeArgs {
+  const void* q;                 // [B, Hq, 128]
+  const uint8_t* k_pages;
+  const uint8_t* v_pages;
+  const int32_t* block_table;    // [B, max_blocks_per_seq]
+  const int32_t* seq_lens;       // [B]
+  float* part_acc;               // [B, Hq, S, 128]  rotated, normalised, x v_scale
+  float* part_lse;               // [B, Hq, S]       log2-sum-exp2 of the split
+  int64_t k_page_bytes;
+  int64_t v_page_bytes;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;                 // num_q_heads / num_kv_heads
+  int32_t k_row_bytes;
+  int32_t v_row_bytes;
+  int32_t max_blocks_per_seq;
+  int32_t pages_per_split;
+  int32_t num_splits;
+  float q_scale;                 // softmax scale * log2(e) / sqrt(128)
+  uint32_t sign_bits[kHeadDim / 32];
+  float k_cent[32];              // fp32 centroids of K (2^k_bits)
+  float v_cent[32];              // fp32 centroids of V, times v_scale
+};
+
+// Arguments of the split-merge + inverse-rotation kernel.
+struct MergeArgs {
+  const float* part_acc;
+  const float* part_lse;
+  const int32_t* seq_lens;
+  float* out;                    // [B, Hq, 128]
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t pages_per_split;
+  int32_t num_splits;
+  float inv_v_scale_over_sqrt_d; // 1 / (v_scale * sqrt(128))
+  uint32_t sign_bits[kHeadDim / 32];
+};
+
+hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+
+}  // namespace tq

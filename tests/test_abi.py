@@ -1,0 +1,81 @@
+"""The C ABI library: it loads, exports every declared symbol, and its host-only
+functions agree with the oracle (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_decode_attention_tq_amd import _lib, api
+from tests.conftest import ROOT
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "tq_write_kv" in names and "tq_paged_decode" in names
+    lib = _lib.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_row_bytes():
+    for bits, rb in ((2, 36), (3, 52), (4, 68), (5, 84)):
+        assert api.row_bytes(128, bits) == rb == oracle.row_bytes(128, bits)
+    assert api.row_bytes(0, 4) == 0 and api.row_bytes(128, 9) == 0
+
+
+@pytest.mark.parametrize("d", [3, 4, 16, 64, 128, 256])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5])
+def test_host_codebook_equals_oracle(d, bits):
+    # two independent solvers (long-double recursion vs scipy/mpmath) agree bit for bit
+    c, t = api.codebook(d, bits)
+    _, c32, t64 = oracle.beta_codebook(d, bits)
+    assert np.array_equal(c, c32)
+    assert np.array_equal(t, t64.astype(np.float32))
+
+
+@pytest.mark.parametrize("seed", [0, 42, 7, 2**63 + 5])
+def test_host_signs_equal_oracle(seed):
+    assert np.array_equal(api.rht_signs(seed, 256), oracle.rht_signs(seed, 256))
+
+
+def test_status_strings_and_argument_errors():
+    lib = _lib.lib()
+    assert lib.tq_status_string(0) == b"ok"
+    assert lib.tq_status_string(4) == b"workspace too small"
+    ctx = api.Context(128, 42)
+    h = ctx.handle
+    # these fail validation before any HIP call
+    assert lib.tq_write_kv(h, None, 1, 4, 2, None, 4, 16, None, 7, None, None) == 2  # bits 7
+    assert lib.tq_write_kv(h, None, 1, 4, 2, None, 4, 16, None, 4, None, None) == 1  # null raw
+    assert lib.tq_write_kv(h, None, 9, 4, 2, None, 4, 16, None, 4, None, None) == 1  # bad dtype
+    assert lib.tq_write_kv(h, None, 1, 0, 2, None, 4, 16, None, 4, None, None) == 0  # nothing to do
+    p = ctypes.c_void_p(16)
+    args = dict(batch=2, hq=32, hkv=1)  # group 32 > 16
+    assert lib.tq_paged_decode(h, p, 1, 2, 32, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 2
+    assert lib.tq_paged_decode(h, p, 1, 2, 6, 4, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 1
+    assert lib.tq_paged_decode(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 32, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 2
+    assert lib.tq_paged_decode(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 16, None) == 4
+    assert lib.tq_paged_decode(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 3, p, 64, 0.0, p, p, 1 << 20, None) == 1
+    odd = ctypes.c_void_p(18)
+    assert lib.tq_paged_decode(h, p, 1, 2, 8, 2, odd, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 3
+    with pytest.raises(ValueError):
+        _lib.check(2, "x")
+    with pytest.raises(_lib.TQError):
+        _lib.check(4, "x")
+    del args
+
+
+def test_context_rejects_other_head_dims():
+    with pytest.raises(ValueError):
+        api.Context(64, 42)

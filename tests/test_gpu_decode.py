@@ -1,0 +1,149 @@
+"""GPU parity of the paged decode (tq_paged_decode) against the oracle.
+
+Each case runs the decode on pages written by the oracle (isolating the
+decode) and on pages written by the GPU writer (the whole path), and checks
+max-abs <= 2e-3 and rel-L2 <= 1e-3 against the oracle's output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_decode_attention_tq_amd import api, workloads
+from tests.parity import compare_decode
+
+pytestmark = pytest.mark.gpu
+
+_TORCH = {np.float16: torch.float16, np.float32: torch.float32}
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    return api.Context(128, 42)
+
+
+def _oracle_pipeline(w):
+    codec = oracle.OracleCodec(w.head_dim, w.rht_seed)
+    kraw, vraw = w.rows("k"), w.rows("v")
+    kp, _ = codec.write_kv(kraw, w.zero_pages(w.k_bits), w.slots, w.k_bits)
+    vp, _ = codec.write_kv(vraw, w.zero_pages(w.v_bits), w.slots, w.v_bits)
+    return codec, kraw, vraw, kp, vp
+
+
+def _decode(ctx, w, q, kp, vp, scale=None):
+    out = api.paged_decode(
+        ctx, q, kp, vp, torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda(),
+        w.k_bits, w.v_bits, max_seq_len=w.max_seq_len, scale=scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _run(ctx, w, scale=None, q_dtype=None, gpu_write=True):
+    print(f"[decode] {w.name} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+          f"K{w.k_bits}V{w.v_bits} lens={w.seq_lens[:8].tolist()} scale={scale}", flush=True)
+    codec, kraw, vraw, kp, vp = _oracle_pipeline(w)
+    q = w.queries()
+    ref = oracle.paged_decode(q, kp, vp, w.block_table, w.seq_lens, w.k_bits, w.v_bits, codec.signs,
+                              codec.centroids32(w.k_bits), codec.centroids32(w.v_bits), scale)
+    qt = torch.from_numpy(q).cuda()
+    if q_dtype is not None:
+        qt = qt.to(q_dtype)
+        ref = oracle.paged_decode(qt.float().cpu().numpy(), kp, vp, w.block_table, w.seq_lens, w.k_bits,
+                                  w.v_bits, codec.signs, codec.centroids32(w.k_bits),
+                                  codec.centroids32(w.v_bits), scale)
+    out = _decode(ctx, w, qt, torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda(), scale)
+    r1 = compare_decode(out, ref, f"{w.name} oracle pages")
+    r2 = None
+    if gpu_write:
+        kpg = torch.zeros(w.page_shape(w.k_bits), dtype=torch.uint8, device="cuda")
+        vpg = torch.zeros(w.page_shape(w.v_bits), dtype=torch.uint8, device="cuda")
+        slots = torch.from_numpy(w.slots).cuda()
+        api.write_kv(ctx, torch.from_numpy(kraw).cuda(), kpg, slots, w.k_bits)
+        api.write_kv(ctx, torch.from_numpy(vraw).cuda(), vpg, slots, w.v_bits)
+        out2 = _decode(ctx, w, qt, kpg, vpg, scale)
+        r2 = compare_decode(out2, ref, f"{w.name} gpu pages")
+    print(f"  max|d| relL2 oracle-pages {r1}  gpu-pages {r2}", flush=True)
+    return out, ref
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (4, 2), (3, 3), (5, 5), (2, 5), (5, 3), (2, 2)])
+def test_bits_combinations(ctx, kb, vb):
+    w = workloads.make_workload(f"bits{kb}{vb}", k_bits=kb, v_bits=vb, num_q_heads=16, num_kv_heads=2,
+                                seq_lens=[300, 17, 1, 64, 0, 129], seed=kb * 10 + vb, lognormal_sigma=0.5)
+    _run(ctx, w)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16])
+def test_group_sizes(ctx, G):
+    w = workloads.make_workload(f"group{G}", num_q_heads=2 * G, num_kv_heads=2, seq_lens=[200, 45, 16],
+                                seed=G, outlier_frac=0.02)
+    _run(ctx, w)
+
+
+def test_many_splits_and_ragged_tails(ctx):
+    # long enough for many 16-page splits per sequence, with ragged last pages
+    w = workloads.make_workload("splits", num_q_heads=8, num_kv_heads=1, seq_lens=[9000, 4097, 255, 16, 15],
+                                seed=5, extra_blocks=5)
+    _run(ctx, w)
+
+
+def test_tiny_preset(ctx):
+    _run(ctx, workloads.preset("tiny"))
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("pages_geometry", dict(batch=3, seq_len=600)),
+    ("mixed_bits", dict(batch=3, seq_len=700)),
+    ("long_context", dict(batch=1, seq_len=5000)),
+    ("ragged_write", dict(batch=6, len_range=(1, 3000))),
+])
+def test_presets_at_reduced_size(ctx, name, kw):
+    _run(ctx, workloads.preset(name, **kw))
+
+
+@pytest.mark.parametrize("q_dtype", [torch.float32, torch.bfloat16])
+def test_query_dtypes(ctx, q_dtype):
+    w = workloads.make_workload("qdt", num_q_heads=8, num_kv_heads=2, seq_lens=[100, 33], seed=9)
+    _run(ctx, w, q_dtype=q_dtype, gpu_write=False)
+
+
+def test_scale_override(ctx):
+    w = workloads.make_workload("scale", num_q_heads=8, num_kv_heads=2, seq_lens=[100, 33], seed=10)
+    _run(ctx, w, scale=0.3)
+
+
+def test_zero_and_single_token_sequences(ctx):
+    w = workloads.make_workload("edge", num_q_heads=4, num_kv_heads=2, seq_lens=[0, 1, 0, 2], seed=12)
+    out, ref = _run(ctx, w)
+    assert not out[0].any() and not out[2].any()
+
+
+def test_large_and_small_norms(ctx):
+    # values far from unit scale: weights must neither overflow nor lose precision
+    for sigma, scale_raw in ((3.0, 1.0), (0.5, 3e3), (0.5, 1e-3)):
+        w = workloads.make_workload("norms", num_q_heads=8, num_kv_heads=2, seq_lens=[150, 40], seed=13,
+                                    dtype=np.float32, lognormal_sigma=sigma)
+        codec = oracle.OracleCodec(128, 42)
+        kraw = w.rows("k") * np.float32(scale_raw)
+        vraw = w.rows("v") * np.float32(scale_raw)
+        kp, _ = codec.write_kv(kraw, w.zero_pages(4), w.slots, 4)
+        vp, _ = codec.write_kv(vraw, w.zero_pages(4), w.slots, 4)
+        q = w.queries() / np.float32(max(scale_raw, 1.0))
+        ref = oracle.paged_decode(q, kp, vp, w.block_table, w.seq_lens, 4, 4, codec.signs,
+                                  codec.centroids32(4), codec.centroids32(4))
+        out = _decode(ctx, w, torch.from_numpy(q).cuda(), torch.from_numpy(kp).cuda(),
+                      torch.from_numpy(vp).cuda())
+        # compare relative to the output scale
+        s = max(1.0, float(np.abs(ref).max()))
+        compare_decode(out / s, ref / s, f"norms sigma={sigma} x{scale_raw}")
+
+
+def test_repeated_calls_are_deterministic(ctx):
+    w = workloads.make_workload("det", num_q_heads=16, num_kv_heads=2, seq_lens=[700, 300], seed=14)
+    codec, _, _, kp, vp = _oracle_pipeline(w)
+    q = torch.from_numpy(w.queries()).cuda()
+    kpt, vpt = torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda()
+    a = _decode(ctx, w, q, kpt, vpt)
+    b = _decode(ctx, w, q, kpt, vpt)
+    assert np.array_equal(a, b)
