@@ -21,8 +21,13 @@ NEAR_FRACTION = 1e-4
 
 
 def compare_pages(gpu_pages: np.ndarray, ref_pages: np.ndarray, near: np.ndarray, bits: int,
-                  written_rows: int, d: int = 128):
-    """Assert the page bytes match the oracle's; returns (mismatched indices, total)."""
+                  written_rows: int, d: int = 128, check_fraction: bool = True):
+    """Assert the page bytes match the oracle's; returns (mismatched indices, total).
+
+    ``check_fraction=False`` drops the 1e-4 bound on the number of
+    near-boundary mismatches (for hand-made rows that sit on boundaries by
+    construction); a mismatch away from a boundary always fails.
+    """
     assert gpu_pages.shape == ref_pages.shape
     ib = oracle.index_bytes(d, bits)
     # norm bytes: exact
@@ -40,7 +45,8 @@ def compare_pages(gpu_pages: np.ndarray, ref_pages: np.ndarray, near: np.ndarray
     assert not np.any(diff & ~near), f"index mismatch away from a boundary at {np.argwhere(diff & ~near)[:5].tolist()}"
     n_bad = int(diff.sum())
     total = written_rows * d
-    assert n_bad < NEAR_FRACTION * total, f"{n_bad} near-boundary mismatches of {total}"
+    if check_fraction:
+        assert n_bad < NEAR_FRACTION * total, f"{n_bad} near-boundary mismatches of {total}"
     return n_bad, total
 
 

@@ -31,11 +31,11 @@ def _gpu_write(ctx, raw, pages, slots, bits, err=None, check=True):
     return pages_t.cpu().numpy()
 
 
-def _check(ctx, codec, raw_np, pages0, slots, bits, raw_gpu=None):
+def _check(ctx, codec, raw_np, pages0, slots, bits, raw_gpu=None, check_fraction=True):
     ref, near = codec.write_kv(raw_np, pages0, slots, bits)
     got = _gpu_write(ctx, raw_np if raw_gpu is None else raw_gpu, pages0, slots, bits)
     written = int((slots >= 0).sum()) * raw_np.shape[1]
-    return compare_pages(got, ref, near, bits, written)
+    return compare_pages(got, ref, near, bits, written, check_fraction=check_fraction)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 5])
@@ -85,7 +85,10 @@ def _special_rows(dtype):
 def test_write_special_rows(ctx, codec, bits, dtype):
     x = _special_rows(dtype)
     pages0 = np.zeros((1, 8, 1, oracle.row_bytes(128, bits)), np.uint8)
-    _check(ctx, codec, x, pages0, np.arange(8, dtype=np.int64), bits)
+    # structured rows put rotated coordinates on or next to boundaries by
+    # construction, so only the placement of mismatches is checked here
+    n_bad, _ = _check(ctx, codec, x, pages0, np.arange(8, dtype=np.int64), bits, check_fraction=False)
+    print(f"[special rows] bits={bits} {np.dtype(dtype).name}: near-boundary mismatches {n_bad}")
     _, n32, _, _ = codec.encode(x[1], bits)
     assert n32[0] == np.float32(1.0)  # the tie rounds to even
 
