@@ -3,7 +3,8 @@
     python -m paged_decode_attention_tq_amd.build
 
 Compiles ``csrc/tq_host.cpp`` (host C++: the C ABI, context, codebook
-solver) and ``csrc/tq_kernels.hip`` (gfx950 kernels) with hipcc into
+solver), ``csrc/tq_write.hip`` (row writer) and ``csrc/tq_decode.hip``
+(paged decode and merge) for gfx950 with hipcc into
 ``paged_decode_attention_tq_amd/libtq.so``.
 """
 
@@ -43,7 +44,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     tmp = LIB + ".tmp"
     cmds = []
-    for src in ("tq_host.cpp", "tq_kernels.hip"):
+    for src in ("tq_host.cpp", "tq_write.hip", "tq_decode.hip"):
         obj = os.path.join(CSRC, src + ".o")
         cmds.append([hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)

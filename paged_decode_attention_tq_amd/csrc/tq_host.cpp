@@ -27,7 +27,7 @@ struct tq_ctx {
   uint32_t sign_bits[kHeadDim / 32];
   float cent[6][32];     // [bits][j], bits 1..5
   float bound[6][31];
-  float v_scale[6];      // fp16-friendly scale of the value centroids per bits
+  float tab_scale[6];    // fp16-friendly scale of the centroid tables per bits
 };
 
 namespace {
@@ -220,26 +220,45 @@ int device_cu_count() {
   return cache[dev];
 }
 
-// Decode work split: every (sequence, KV head) is cut into splits of
-// pages_per_split pages, one wave each.
+// Decode work split.  A workgroup covers heads_per_wg KV heads (the largest
+// divisor of num_kv_heads up to 8) and pages_per_split pages of one sequence;
+// its waves are heads_per_wg x streams, streams = 8 / heads_per_wg page
+// streams per head.  The split count aims at one full round of two
+// workgroups per CU, keeps at least 8 splits for the longest sequence (so
+// ragged batches balance) and at most 64 splits (the merge holds one split
+// weight per lane).
 struct SplitPlan {
+  int heads_per_wg;
+  int streams;
+  int head_groups;
   int pages_per_split;
   int num_splits;
 };
 
 SplitPlan plan_split(int batch, int num_kv_heads, int max_seq_len, int num_cus) {
-  const int max_pages = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
   SplitPlan p;
+  p.heads_per_wg = 1;
+  for (int h = 1; h <= 8; ++h)
+    if (num_kv_heads % h == 0) p.heads_per_wg = h;
+  p.streams = 8 / p.heads_per_wg;
+  if (p.streams < 1) p.streams = 1;
+  p.head_groups = num_kv_heads / p.heads_per_wg;
+  const int max_pages = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
   if (max_pages <= 0) {
     p.pages_per_split = 1;
     p.num_splits = 1;
     return p;
   }
-  const long long work = (long long)batch * num_kv_heads * max_pages;
-  const long long target_waves = (long long)num_cus * 32;
-  long long pps = (work + target_waves - 1) / target_waves;
-  if (pps < 16) pps = 16;
-  if (pps > max_pages) pps = max_pages;
+  const long long units = (long long)batch * p.head_groups;
+  const long long target = 2LL * num_cus;
+  long long s0 = (target + units - 1) / units;
+  if (s0 < 1) s0 = 1;
+  long long pps = (max_pages + s0 - 1) / s0;
+  const long long cap = (max_pages + 7) / 8;
+  if (pps > cap) pps = cap;
+  const long long floor_pps = (max_pages + 63) / 64;
+  if (pps < floor_pps) pps = floor_pps;
+  if (pps < 1) pps = 1;
   p.pages_per_split = (int)pps;
   p.num_splits = (int)((max_pages + pps - 1) / pps);
   return p;
@@ -298,7 +317,7 @@ tq_status tq_ctx_create(int head_dim, uint64_t rht_seed, tq_ctx** out) {
     if (c->signs[i] < 0) c->sign_bits[i >> 5] |= 1u << (i & 31);
   for (int b = 1; b <= 5; ++b) {
     solve_codebook(head_dim, b, c->cent[b], c->bound[b]);
-    c->v_scale[b] = best_fp16_scale(c->cent[b], 1 << b);
+    c->tab_scale[b] = best_fp16_scale(c->cent[b], 1 << b);
   }
   *out = c;
   return TQ_OK;
@@ -376,7 +395,8 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
 
   SplitPlan p = plan_split(batch, num_kv_heads, max_seq_len, device_cu_count());
   const float sm_scale = scale > 0 ? scale : 1.0f / std::sqrt((float)kHeadDim);
-  const float v_scale = ctx->v_scale[v_bits];
+  const float k_scale = ctx->tab_scale[k_bits];
+  const float v_scale = ctx->tab_scale[v_bits];
 
   tq::DecodeArgs d;
   std::memset(&d, 0, sizeof(d));
@@ -396,11 +416,14 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   d.num_kv_heads = num_kv_heads;
   d.group = group;
   d.max_blocks_per_seq = max_blocks_per_seq;
+  d.heads_per_wg = p.heads_per_wg;
+  d.streams = p.streams;
+  d.head_groups = p.head_groups;
   d.pages_per_split = p.pages_per_split;
   d.num_splits = p.num_splits;
-  d.q_scale = (float)((double)sm_scale * 1.4426950408889634 / std::sqrt((double)kHeadDim));
+  d.q_scale = (float)((double)sm_scale * 1.4426950408889634 / (std::sqrt((double)kHeadDim) * k_scale));
   std::memcpy(d.sign_bits, ctx->sign_bits, sizeof(d.sign_bits));
-  for (int j = 0; j < (1 << k_bits); ++j) d.k_cent[j] = ctx->cent[k_bits][j];
+  for (int j = 0; j < (1 << k_bits); ++j) d.k_cent[j] = ctx->cent[k_bits][j] * k_scale;
   for (int j = 0; j < (1 << v_bits); ++j) d.v_cent[j] = ctx->cent[v_bits][j] * v_scale;
 
   tq_status st = hip_status(tq::launch_decode(d, (int)q_dtype, k_bits, v_bits, (hipStream_t)stream));

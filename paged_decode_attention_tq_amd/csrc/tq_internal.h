@@ -27,7 +27,10 @@ struct WriteArgs {
   float pos_bounds[16];     // the 2^(b-1) - 1 positive boundaries, increasing
 };
 
-// Arguments of the decode split kernel.
+// Arguments of the decode split kernel.  One workgroup handles one
+// (sequence, group of heads_per_wg KV heads, split) and runs
+// heads_per_wg * streams waves: each wave owns one KV head and every
+// streams-th page of the split, so the workgroup consumes whole pages.
 struct DecodeArgs {
   const void* q;                 // [B, Hq, 128]
   const uint8_t* k_pages;
@@ -45,12 +48,15 @@ struct DecodeArgs {
   int32_t k_row_bytes;
   int32_t v_row_bytes;
   int32_t max_blocks_per_seq;
-  int32_t pages_per_split;
-  int32_t num_splits;
-  float q_scale;                 // softmax scale * log2(e) / sqrt(128)
+  int32_t heads_per_wg;          // KV heads per workgroup (divides num_kv_heads)
+  int32_t streams;               // page streams per head in a workgroup
+  int32_t head_groups;           // num_kv_heads / heads_per_wg
+  int32_t pages_per_split;       // pages per workgroup
+  int32_t num_splits;            // S
+  float q_scale;                 // softmax scale * log2(e) / (sqrt(128) * k_scale)
   uint32_t sign_bits[kHeadDim / 32];
-  float k_cent[32];              // fp32 centroids of K (2^k_bits)
-  float v_cent[32];              // fp32 centroids of V, times v_scale
+  float k_cent[32];              // fp32 centroids of K times k_scale
+  float v_cent[32];              // fp32 centroids of V times v_scale
 };
 
 // Arguments of the split-merge + inverse-rotation kernel.

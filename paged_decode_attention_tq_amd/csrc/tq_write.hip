@@ -1,0 +1,190 @@
+// Row writer kernel for gfx950: encodes raw K or V rows into TQ rows and
+// stores them in the uint8 pages through flat slots.
+//
+// Row format: TurboQuant docs, "vLLM Usage" section "TQ Byte Layout"
+// (ceil(128*bits/8) bytes of LSB-first packed codebook indices, then the
+// fp32 norm); slots: "vLLM Usage" section "Slot Mapping" (negative slots are
+// ignored, out-of-range slots are an error); pages: "Architecture" section
+// "Cache Storage Objects" ([num_blocks, block_size, num_kv_heads, row_bytes]).
+
+#include "tq_internal.h"
+#include "tq_device.h"
+
+namespace tq {
+
+// ==========================================================================
+// Row writer: one row (token, head) per 4-lane quad, 32 elements per lane.
+//
+// Per row: n = fp32(sqrt(sum x^2)) with the sum exact-rounded in float64
+// (fast path: plain float64 accumulation; when the error bound does not
+// decide the fp32 rounding, the row is re-summed with double-double
+// arithmetic); r = H (s * x) / (n sqrt(128)); idx = nearest centroid via the
+// symmetric boundary count; LSB-first pack; store at the slot.
+// ==========================================================================
+
+template <int DT>
+__device__ __forceinline__ void load_row32(const void* raw, int64_t elem_off, float (&x)[32]) {
+  if constexpr (DT == 0) {  // fp32: 8 x 16 bytes
+    const float* p = static_cast<const float*>(raw) + elem_off;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(p + 4 * i);
+      x[4 * i + 0] = __uint_as_float(v.x);
+      x[4 * i + 1] = __uint_as_float(v.y);
+      x[4 * i + 2] = __uint_as_float(v.z);
+      x[4 * i + 3] = __uint_as_float(v.w);
+    }
+  } else {  // fp16 / bf16: 4 x 16 bytes
+    const uint16_t* p = static_cast<const uint16_t*>(raw) + elem_off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(p + 8 * i);
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint16_t lo = (uint16_t)(w[k] & 0xFFFF), hi = (uint16_t)(w[k] >> 16);
+        if constexpr (DT == 1) {
+          x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, lo);
+          x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, hi);
+        } else {
+          x[8 * i + 2 * k] = bf16_to_f32(lo);
+          x[8 * i + 2 * k + 1] = bf16_to_f32(hi);
+        }
+      }
+    }
+  }
+}
+
+template <int BITS, int DT>
+__global__ __launch_bounds__(256) void write_rows_kernel(WriteArgs a) {
+  constexpr int N = 1 << BITS;
+  constexpr int HALF = N / 2;
+  const int q = threadIdx.x & 3;
+  const int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  if (row >= a.num_rows) return;  // uniform per quad
+  const int64_t tok = row / a.num_kv_heads;
+  const int head = (int)(row - tok * a.num_kv_heads);
+  const int64_t slot = a.slots[tok];
+  if (slot < 0) return;
+  if (slot >= a.num_slots) {
+    if (q == 0 && head == 0 && a.err_count) atomicAdd(a.err_count, 1);
+    return;
+  }
+
+  float x[32];
+  load_row32<DT>(a.raw, row * kHeadDim + 32 * q, x);
+
+  // ---- norm: float64 sum of squares, exact-rounded ------------------------
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) s = __builtin_fma((double)x[j], (double)x[j], s);
+  s += quad_xor<1>(s);
+  s += quad_xor<2>(s);
+  double n64 = sqrt_rn(s);
+  {
+    // the fast sum has relative error below 40 * 2^-53; the sqrt halves it
+    const double lo = n64 * (1.0 - 0x1p-47), hi = n64 * (1.0 + 0x1p-47);
+    if ((float)lo != (float)hi) {
+      double sh = 0.0, sl = 0.0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        double sq = (double)x[j] * (double)x[j];  // exact
+        double t, e;
+        two_sum(sh, sq, t, e);
+        sh = t;
+        sl += e;
+      }
+      {
+        double oh = quad_xor<1>(sh), ol = quad_xor<1>(sl), t, e;
+        two_sum(sh, oh, t, e);
+        sh = t;
+        sl = sl + ol + e;
+      }
+      {
+        double oh = quad_xor<2>(sh), ol = quad_xor<2>(sl), t, e;
+        two_sum(sh, oh, t, e);
+        sh = t;
+        sl = sl + ol + e;
+      }
+      n64 = sqrt_rn(sh + sl);
+    }
+  }
+  const float n32 = (float)n64;
+  const float c = n64 > 0.0 ? (float)(1.0 / (n64 * 11.313708498984761)) : 0.0f;  // 1/(n sqrt(128))
+
+  // ---- randomized Hadamard transform ------------------------------------
+  const uint32_t sw = a.sign_bits[q];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((sw >> j) & 1u) << 31));
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if ((j & h) == 0) {
+        const float u = x[j], v = x[j + h];
+        x[j] = u + v;
+        x[j + h] = u - v;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float p = quad_xor<1>(x[j]);
+    x[j] = (q & 1) ? p - x[j] : x[j] + p;
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float p = quad_xor<2>(x[j]);
+    x[j] = (q & 2) ? p - x[j] : x[j] + p;
+  }
+
+  // ---- nearest centroid and LSB-first packing ----------------------------
+  uint32_t w[BITS];
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) w[k] = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const float r = x[j] * c;
+    const float ar = __builtin_fabsf(r);
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < HALF - 1; ++k) cnt += (ar > a.pos_bounds[k]) ? 1 : 0;
+    const uint32_t idx = (uint32_t)(r > 0.0f ? HALF + cnt : HALF - 1 - cnt);
+    const int pos = BITS * j;
+    w[pos >> 5] |= idx << (pos & 31);
+    if ((pos & 31) + BITS > 32) w[(pos >> 5) + 1] |= idx >> (32 - (pos & 31));
+  }
+
+  uint8_t* dst = a.pages + (slot / a.block_size) * a.page_bytes +
+                 ((slot % a.block_size) * a.num_kv_heads + head) * (int64_t)a.row_bytes;
+  uint32_t* d32 = reinterpret_cast<uint32_t*>(dst) + BITS * q;
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) d32[k] = w[k];
+  if (q == 3) *reinterpret_cast<float*>(dst + a.row_bytes - 4) = n32;
+}
+
+template <int BITS>
+static hipError_t launch_write_bits(const WriteArgs& a, int dt, hipStream_t st) {
+  const dim3 grid((unsigned)((a.num_rows + 63) / 64)), block(256);
+  if (dt == 0)
+    hipLaunchKernelGGL((write_rows_kernel<BITS, 0>), grid, block, 0, st, a);
+  else if (dt == 1)
+    hipLaunchKernelGGL((write_rows_kernel<BITS, 1>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((write_rows_kernel<BITS, 2>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t stream) {
+  if (a.num_rows == 0) return hipSuccess;
+  switch (bits) {
+    case 2: return launch_write_bits<2>(a, raw_dtype, stream);
+    case 3: return launch_write_bits<3>(a, raw_dtype, stream);
+    case 4: return launch_write_bits<4>(a, raw_dtype, stream);
+    case 5: return launch_write_bits<5>(a, raw_dtype, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+
+}  // namespace tq

@@ -121,7 +121,8 @@ def test_zero_and_single_token_sequences(ctx):
 
 def test_large_and_small_norms(ctx):
     # values far from unit scale: weights must neither overflow nor lose precision
-    for sigma, scale_raw in ((3.0, 1.0), (0.5, 3e3), (0.5, 1e-3)):
+    for sigma, scale_raw, q_mul in ((3.0, 1.0, 1.0), (0.5, 3e3, 1 / 3e3), (0.5, 1e-3, 1.0), (1.0, 1.0, 40.0),
+                                    (0.5, 1.0, 1e-4)):
         w = workloads.make_workload("norms", num_q_heads=8, num_kv_heads=2, seq_lens=[150, 40], seed=13,
                                     dtype=np.float32, lognormal_sigma=sigma)
         codec = oracle.OracleCodec(128, 42)
@@ -129,14 +130,15 @@ def test_large_and_small_norms(ctx):
         vraw = w.rows("v") * np.float32(scale_raw)
         kp, _ = codec.write_kv(kraw, w.zero_pages(4), w.slots, 4)
         vp, _ = codec.write_kv(vraw, w.zero_pages(4), w.slots, 4)
-        q = w.queries() / np.float32(max(scale_raw, 1.0))
+        q = w.queries() * np.float32(q_mul)
         ref = oracle.paged_decode(q, kp, vp, w.block_table, w.seq_lens, 4, 4, codec.signs,
                                   codec.centroids32(4), codec.centroids32(4))
         out = _decode(ctx, w, torch.from_numpy(q).cuda(), torch.from_numpy(kp).cuda(),
                       torch.from_numpy(vp).cuda())
         # compare relative to the output scale
-        s = max(1.0, float(np.abs(ref).max()))
-        compare_decode(out / s, ref / s, f"norms sigma={sigma} x{scale_raw}")
+        s = float(np.abs(ref).max()) or 1.0
+        r = compare_decode(out / s, ref / s, f"norms sigma={sigma} x{scale_raw} q*{q_mul}")
+        print(f"  norms sigma={sigma} x{scale_raw} q*{q_mul}: {r}", flush=True)
 
 
 def test_repeated_calls_are_deterministic(ctx):
