@@ -31,6 +31,10 @@ HIP_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# per-source extras: the decode never produces NaNs on valid input, so it
+# drops IEEE NaN quieting (fmaxf then needs no canonicalisation)
+EXTRA_FLAGS = {"tq_decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+
 
 def hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -46,7 +50,8 @@ def build(verbose: bool = False) -> str:
     cmds = []
     for src in ("tq_host.cpp", "tq_write.hip", "tq_decode.hip"):
         obj = os.path.join(CSRC, src + ".o")
-        cmds.append([hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     cmds.append([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     for cmd in cmds:

@@ -35,6 +35,8 @@
 #include "tq_internal.h"
 #include "tq_device.h"
 
+#include <type_traits>
+
 namespace tq {
 
 // ---------------------------------------------------------------------------
@@ -118,7 +120,7 @@ struct PageRegs {
 
 constexpr int kMaxWaves = 8;
 
-template <int KB, int VB, int QT, bool PACK>
+template <int KB, int VB, int QT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_split_kernel(DecodeArgs a) {
   using KT = PairTable<KB>;
   using VT = PairTable<VB>;
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   constexpr int kVBase = 0;
   constexpr int kKBase = kShareV ? 0 : VT::kBytes;
   constexpr int kTabBytes = kKBase + KT::kBytes;
-  constexpr int kMergeBytes = kMaxWaves * 16 * (kHeadDim + 2) * 4;
+  constexpr int kMergeBytes = kMaxWaves * 8 * (kHeadDim + 2) * 4;
   constexpr int kLds = kTabBytes > kMergeBytes ? kTabBytes : kMergeBytes;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
 
@@ -145,28 +147,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if constexpr (!kShareV) fill_pair_table<VB>(lds + kVBase, a.v_cent);
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6;
+  // the wave index is uniform; say so, so that everything derived from it
+  // (head, page stream, page addresses) lives in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int gl = wave % a.heads_per_wg;
   const int st = wave / a.heads_per_wg;
-  const int g = hg * a.heads_per_wg + gl;
+  const int gv = hg * a.heads_per_wg + gl;     // virtual head: (KV head, group of <= 8 query heads)
+  const int g = gv / a.q_groups;               // KV head
+  const int qh0 = g * a.group + (gv % a.q_groups) * 8;
+  const int gsz = min(8, a.group - (gv % a.q_groups) * 8);  // query heads of this wave
   const int n = lane & 15;
   const int c = lane >> 4;
-  const int G = a.group;
+  const int hq = n & 7;                        // query head (within the wave's group) of column n
+  const int par = n >> 3;                      // column half: q_lo / odd value dims
   const int span = p1 - p0;
   const int nw = span > st ? (span - st + a.streams - 1) / a.streams : 0;
 
-  // ---- rotated, scaled query in the B-operand layout --------------------
-  // lane (n, c) holds dims 32c..32c+31 of column n; PACK: columns 0..7 hold
-  // q_hi of heads 0..7 of the group, columns 8..15 their q_lo.
-  half8 qb[4];
-  half8 qb_lo[PACK ? 1 : 4];
-  float q_unscale;  // scores come out multiplied by 1 / q_unscale
+  // ---- rotated, scaled query as the B operand of the score MFMAs ----------
+  // Lane (n, c) covers dims 32c..32c+31 (16 pairs); column n < 8 holds the
+  // fp16 hi part of head n, column n + 8 its lo part.  MFMA m takes pairs
+  // 2m and 2m+1, each twice (the A operand interleaves K hi and K lo).
+  uint32_t qd[16];   // dword = fp16 pair (dims 2p, 2p+1) of this lane's column
+  float q_unscale;   // scores come out multiplied by 1 / q_unscale
   {
-    const int hq = PACK ? (n & 7) : n;
-    const bool has = hq < G;
-    // columns past the group read head 0 of the group and are zeroed
-    const int64_t qoff = ((int64_t)b * a.num_q_heads + (int64_t)g * G + (has ? hq : 0)) * kHeadDim + 32 * c;
+    const bool has = hq < gsz;
+    const int64_t qoff = ((int64_t)b * a.num_q_heads + qh0 + (has ? hq : 0)) * kHeadDim + 32 * c;
     float x[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) x[j] = load_q<QT>(a.q, qoff + j);
@@ -207,19 +213,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const float up = __builtin_ldexpf(a.q_scale, 11 - qe);
     q_unscale = __builtin_ldexpf(1.0f, qe - 11);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int p = 0; p < 16; ++p) {
+      _Float16 h2[2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = x[8 * m + j] * up;
+      for (int e = 0; e < 2; ++e) {
+        const float v = x[2 * p + e] * up;
         const _Float16 hi = (_Float16)v;
-        const _Float16 lo = (_Float16)(v - (float)hi);
-        if constexpr (PACK) {
-          qb[m][j] = (n < 8) ? hi : lo;
-        } else {
-          qb[m][j] = hi;
-          qb_lo[m][j] = lo;
-        }
+        h2[e] = par ? (_Float16)(v - (float)hi) : hi;
       }
+      qd[p] = pack_half2(h2[0], h2[1]);
+    }
   }
 
   // ---- per-lane byte offsets inside a page --------------------------------
@@ -229,91 +232,116 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const int k_norm_off = 4 * c * k_tok + g * a.k_row_bytes + a.k_row_bytes - 4;  // + r * k_tok
   const int v_byte = n * VB;
   const int v_row = 4 * c * v_tok + g * a.v_row_bytes;                            // + j * v_tok
-  const int v_dat_off = v_row + ((VB == 3 || VB == 5) ? (v_byte & ~3) : v_byte);
+  const int v_dat_off = v_row + ((VB == 3 || VB == 5) ? (v_byte & ~3) : (v_byte & ~1));
   const int v_norm_off = v_row + a.v_row_bytes - 4;
   const uint32_t v_shift = 8u * (uint32_t)(v_byte & 3);
   const uint32_t k_lane = (uint32_t)(lane & (KT::kRep - 1)) * 4u;
   const uint32_t v_lane = (uint32_t)(lane & (VT::kRep - 1)) * 4u;
   const uint8_t* k_tab = lds + kKBase;
   const uint8_t* v_tab = kShareV ? (lds + kKBase) : (lds + kVBase);
+  const uint32_t w_shift = 16u * (uint32_t)par;  // weight half: even dims in columns < 8
 
-  // ---- block ids: lane j holds the id of this wave's page 64*chunk + j ----
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0 + st;
-  const int stride_p = a.streams;
-  auto load_ids = [&](int chunk) -> int {
-    const int i = 64 * chunk + lane;
-    return i < nw ? bt[(int64_t)i * stride_p] : 0;
-  };
-  int ids0 = load_ids(0);
-  int ids1 = nw > 64 ? load_ids(1) : 0;
-  int id_chunk = 0;
-  auto block_of = [&](int i) -> int {
-    if ((i >> 6) != id_chunk) {  // once every 64 pages, uniform
-      ids0 = ids1;
-      ++id_chunk;
-      ids1 = (nw > 64 * (id_chunk + 1)) ? load_ids(id_chunk + 1) : 0;
-    }
-    return __builtin_amdgcn_readlane(ids0, i & 63);
-  };
+  // ---- page walk ------------------------------------------------------------
+  const int32_t* __restrict__ bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0 + st;
+  const int strm = a.streams;
+  const int nwu = __builtin_amdgcn_readfirstlane(nw);
+  const int page_base = p0 + st;
 
-  auto load_page = [&](PageRegs<KB, VB>& P, int blk) {
-    const uint8_t* kp = a.k_pages + (int64_t)blk * a.k_page_bytes;
-    const uint8_t* vp = a.v_pages + (int64_t)blk * a.v_page_bytes;
+  // page data registers are refilled for the next page as soon as each part
+  // has been consumed, so one page of loads is always in flight
+  PageRegs<KB, VB> P;
+  __amdgpu_buffer_rsrc_t kr, vr;
+  auto set_page = [&](int blk_in) {
+    const int blk = __builtin_amdgcn_readfirstlane(blk_in);
+    kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_pages + (int64_t)blk * a.k_page_bytes),
+                                           (short)0, 0x7FFFFFFF, 0x00020000);
+    vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_pages + (int64_t)blk * a.v_page_bytes),
+                                           (short)0, 0x7FFFFFFF, 0x00020000);
+  };
+  auto load_kw = [&]() {
 #pragma unroll
-    for (int i = 0; i < KB; ++i) P.kw[i] = ld_u32(kp + k_idx_off + 4 * i);
+    for (int i = 0; i < KB; ++i) P.kw[i] = __builtin_amdgcn_raw_buffer_load_b32(kr, k_idx_off, 4 * i, 0);
+  };
+  auto load_nk = [&]() {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) P.nk[r] = ld_f32(kp + r * k_tok + k_norm_off);
+    for (int r = 0; r < 4; ++r)
+      P.nk[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kr, k_norm_off, r * k_tok, 0));
+  };
+  auto load_vw = [&]() {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint8_t* vr = vp + j * v_tok;
       if constexpr (VB == 2) {
-        P.vw[j] = *reinterpret_cast<const uint16_t*>(vr + v_dat_off);
+        P.vw[j] = __builtin_amdgcn_raw_buffer_load_b16(vr, v_dat_off, j * v_tok, 0);
       } else {
-        P.vw[j] = ld_u32(vr + v_dat_off);
-        if constexpr (VB == 3 || VB == 5) P.vw2[j] = ld_u32(vr + v_dat_off + 4);
+        P.vw[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_dat_off, j * v_tok, 0);
+        if constexpr (VB == 3 || VB == 5) P.vw2[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_dat_off, j * v_tok + 4, 0);
       }
-      P.nv[j] = ld_f32(vr + v_norm_off);
     }
   };
-
-  floatx4 acc[8];
+  auto load_nv = [&]() {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+      P.nv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, v_norm_off, j * v_tok, 0));
+  };
+
+  // acc[blk][r]: column n (head hq), dim 32c + 8r + 2blk + par
+  floatx4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -__builtin_inff();
   float l_part = 0.0f;
 
-  auto compute_page = [&](const PageRegs<KB, VB>& P, int i) {
-    const int tok0 = (p0 + st + stride_p * i) * kBlockSize + 4 * c;
-    // -- scores
+  auto compute_page = [&](int i, auto full_tag, auto loads_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    constexpr bool more = decltype(loads_tag)::value;  // refill P for the next page
+    const int tok0 = (page_base + strm * i) * kBlockSize + 4 * c;
+    // -- key lookups: (hi, lo) fp16 pairs of 16 dim pairs, then refill
+    uint32_t kh[16], kl[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t ad = pair_addr<KB>(P.kw, k, k_lane);
+      kh[k] = lds_u32(k_tab, ad);
+      kl[k] = lds_u32(k_tab + KT::kLoOff, ad);
+    }
+    if constexpr (more) load_kw();
+    // -- value lookups: dword (V[t][2p], V[t][2p+1]) for pair p = 4n + blk of
+    // token 4c + j is exactly A[row n][k = 2j, 2j+1] of value block blk
+    uint32_t va[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t words[2];
+      if constexpr (VB == 3 || VB == 5) {
+        const uint64_t all = ((((uint64_t)P.vw2[j]) << 32) | P.vw[j]) >> v_shift;
+        words[0] = (uint32_t)all;
+        words[1] = (uint32_t)(all >> 32);
+      } else {
+        words[0] = P.vw[j];
+        words[1] = 0;
+      }
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) va[blk][j] = lds_u32(v_tab, pair_addr<VB>(words, blk, v_lane));
+    }
+    if constexpr (more) load_vw();
+    // -- scores: A = [K_hi(p), K_lo(p), K_hi(p'), K_lo(p')], B = [q(p), q(p), q(p'), q(p')]
     floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t ah[4], al[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t ad = pair_addr<KB>(P.kw, 4 * m + k, k_lane);
-        ah[k] = lds_u32(k_tab, ad);
-        al[k] = lds_u32(k_tab + KT::kLoOff, ad);
-      }
-      const half8 Ahi = __builtin_bit_cast(half8, u32x4{ah[0], ah[1], ah[2], ah[3]});
-      const half8 Alo = __builtin_bit_cast(half8, u32x4{al[0], al[1], al[2], al[3]});
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, qb[m], sc, 0, 0, 0);
-      if constexpr (!PACK) sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, qb_lo[m], sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, qb[m], sc, 0, 0, 0);
+    for (int m = 0; m < 8; ++m) {
+      const half8 A = __builtin_bit_cast(half8, u32x4{kh[2 * m], kl[2 * m], kh[2 * m + 1], kl[2 * m + 1]});
+      const half8 Bq = __builtin_bit_cast(half8, u32x4{qd[2 * m], qd[2 * m], qd[2 * m + 1], qd[2 * m + 1]});
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq, sc, 0, 0, 0);
     }
-    // -- softmax bookkeeping (log2 domain)
-    float sv[4];
-    float pmax = -__builtin_inff();
+    // -- softmax bookkeeping (log2 domain).  e = an upper bound of log2(n_v)
+    // from the exponent bits (clamped so empty rows cannot blow up p).
+    float full[4], xv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float full = PACK ? sc[r] + row_ror8(sc[r]) : sc[r];
-      const bool valid = tok0 + r < L;
-      sv[r] = valid ? full * (P.nk[r] * q_unscale) : -__builtin_inff();
-      int e = 0;
-      (void)__builtin_frexpf(P.nv[r], &e);
-      const float ev = (P.nv[r] > 0.0f) ? (float)max(e, -64) : -64.0f;
-      pmax = fmaxf(pmax, sv[r] + ev);
+      full[r] = (sc[r] + row_ror8(sc[r])) * (P.nk[r] * q_unscale);
+      const float e = fmaxf(__builtin_fmaf((float)(__float_as_uint(P.nv[r]) >> 24), 2.0f, -126.0f), -64.0f);
+      xv[r] = full[r] + e;
+      if constexpr (!FULL) xv[r] = (tok0 + r < L) ? xv[r] : -__builtin_inff();
     }
+    if constexpr (more) load_nk();
+    float pmax = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
     pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
     pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
     if (__builtin_amdgcn_ballot_w64(pmax > m_ref + 8.0f) != 0) {
@@ -321,97 +349,81 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
       l_part *= alpha;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] *= alpha;
+      for (int q = 0; q < 4; ++q) acc[q] *= alpha;
       m_ref = m_new;
     }
-    half4 W, Wlo;
+    // -- weights w = p * n_v as fp16 hi + lo, placed in this column's half
+    uint32_t whi[4], wlo[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool valid = tok0 + r < L;
-      const float pr = valid ? __builtin_amdgcn_exp2f(sv[r] - m_ref) : 0.0f;
+      float pr = __builtin_amdgcn_exp2f(full[r] - m_ref);
+      if constexpr (!FULL) pr = (tok0 + r < L) ? pr : 0.0f;
       l_part += pr;
-      const float wv = valid ? pr * P.nv[r] : 0.0f;
+      float wv = pr * P.nv[r];
+      if constexpr (!FULL) wv = (tok0 + r < L) ? wv : 0.0f;  // rows past the end may hold anything
       const _Float16 hi = (_Float16)wv;
       const _Float16 lo = (_Float16)(wv - (float)hi);
-      if constexpr (PACK) {
-        W[r] = (n < 8) ? hi : lo;
-      } else {
-        W[r] = hi;
-        Wlo[r] = lo;
-      }
+      whi[r] = (uint32_t)__builtin_bit_cast(uint16_t, hi) << w_shift;
+      wlo[r] = (uint32_t)__builtin_bit_cast(uint16_t, lo) << w_shift;
     }
-    // -- values
+    if constexpr (more) load_nv();
+    const half8 Whi = __builtin_bit_cast(half8, u32x4{whi[0], whi[1], whi[2], whi[3]});
+    const half8 Wlo = __builtin_bit_cast(half8, u32x4{wlo[0], wlo[1], wlo[2], wlo[3]});
+    // -- values: acc[pair][col] += sum_(t, parity) V[t][2 pair + parity] * w[t][head] [parity == col half]
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t L4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t words[2];
-        if constexpr (VB == 3 || VB == 5) {
-          const uint64_t all = ((((uint64_t)P.vw2[j]) << 32) | P.vw[j]) >> v_shift;
-          words[0] = (uint32_t)all;
-          words[1] = (uint32_t)(all >> 32);
-        } else {
-          words[0] = P.vw[j];
-          words[1] = 0;
-        }
-        L4[j] = lds_u32(v_tab, pair_addr<VB>(words, k, v_lane));
-      }
-      // block 2k takes the low halves (dim 8n+2k), block 2k+1 the high halves
-      const uint32_t lo01 = __builtin_amdgcn_perm(L4[1], L4[0], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(L4[3], L4[2], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(L4[1], L4[0], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(L4[3], L4[2], 0x07060302u);
-      const half4 Ae = __builtin_bit_cast(half4, (uint64_t)lo01 | ((uint64_t)lo23 << 32));
-      const half4 Ao = __builtin_bit_cast(half4, (uint64_t)hi01 | ((uint64_t)hi23 << 32));
-      acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ae, W, acc[2 * k], 0, 0, 0);
-      acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ao, W, acc[2 * k + 1], 0, 0, 0);
-      if constexpr (!PACK) {
-        acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ae, Wlo, acc[2 * k], 0, 0, 0);
-        acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(Ao, Wlo, acc[2 * k + 1], 0, 0, 0);
-      }
+    for (int blk = 0; blk < 4; ++blk) {
+      const half8 A = __builtin_bit_cast(half8, u32x4{va[blk][0], va[blk][1], va[blk][2], va[blk][3]});
+      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Whi, acc[blk], 0, 0, 0);
+      acc[blk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Wlo, acc[blk], 0, 0, 0);
     }
   };
 
-  // ---- page loop, one page of prefetch ------------------------------------
-  if (nw > 0) {
-    PageRegs<KB, VB> A, Bq;
-    load_page(A, block_of(0));
-    for (int i = 0; i < nw; i += 2) {
-      load_page(Bq, block_of(min(i + 1, nw - 1)));
-      compute_page(A, i);
-      if (i + 1 >= nw) break;
-      load_page(A, block_of(min(i + 2, nw - 1)));
-      compute_page(Bq, i + 1);
+  // ---- page loop ------------------------------------------------------------------
+  // Only a sequence's last page can be partial; it is peeled off so the loop
+  // body has a single path (no register copies of in-flight loads).
+  if (nwu > 0) {
+    const bool last_full = (page_base + strm * (nwu - 1) + 1) * kBlockSize <= L;
+    const int n_full = last_full ? nwu : nwu - 1;
+    set_page(bt[0]);
+    load_kw();
+    load_vw();
+    load_nk();
+    load_nv();
+    int id_next = bt[(int64_t)min(1, nwu - 1) * strm];
+    for (int i = 0; i < n_full; ++i) {
+      set_page(id_next);  // loads issued inside fetch page i + 1 (the last page again at the end)
+      id_next = bt[(int64_t)min(i + 2, nwu - 1) * strm];
+      compute_page(i, std::true_type{}, std::true_type{});
     }
+    if (!last_full) compute_page(nwu - 1, std::false_type{}, std::false_type{});
   }
 
-  // ---- fold the lo columns, finish the split --------------------------------
-  if constexpr (PACK) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[q][r] += row_ror8(acc[q][r]);
-    }
-  }
+  // ---- finish the split ---------------------------------------------------------
   float l_tot = l_part + __shfl_xor(l_part, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  const int hq = PACK ? (n & 7) : n;
-  const bool owner = (PACK ? n < 8 : true) && hq < G;
+  // gather the odd dims from column n + 8: o[r][d] = dim 32c + 8r + d of head hq
+  float o[4][8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const float mine = acc[blk][r];
+      const float other = row_ror8(mine);
+      o[r][2 * blk] = par ? other : mine;
+      o[r][2 * blk + 1] = par ? mine : other;
+    }
+  const bool owner = par == 0 && hq < gsz;
 
   if (a.streams == 1) {
     if (owner) {
-      const int h = g * G + hq;
+      const int h = qh0 + hq;
       const int64_t slot = ((int64_t)b * a.num_q_heads + h) * S + s;
       const float inv = 1.0f / l_tot;
       float* dst = a.part_acc + slot * kHeadDim + 32 * c;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        floatx4 v0, v1;
-        v0.x = acc[0][r] * inv; v0.y = acc[1][r] * inv; v0.z = acc[2][r] * inv; v0.w = acc[3][r] * inv;
-        v1.x = acc[4][r] * inv; v1.y = acc[5][r] * inv; v1.z = acc[6][r] * inv; v1.w = acc[7][r] * inv;
-        *reinterpret_cast<floatx4*>(dst + 8 * r) = v0;
-        *reinterpret_cast<floatx4*>(dst + 8 * r + 4) = v1;
+        *reinterpret_cast<floatx4*>(dst + 8 * r) = floatx4{o[r][0] * inv, o[r][1] * inv, o[r][2] * inv, o[r][3] * inv};
+        *reinterpret_cast<floatx4*>(dst + 8 * r + 4) = floatx4{o[r][4] * inv, o[r][5] * inv, o[r][6] * inv, o[r][7] * inv};
       }
       if (c == 0) a.part_lse[slot] = m_ref + __builtin_log2f(l_tot);
     }
@@ -420,66 +432,58 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 
   // several streams per head: merge them through LDS (the tables are dead)
   __syncthreads();
-  float* m_buf = reinterpret_cast<float*>(lds);                   // [waves][16]
-  float* l_buf = m_buf + kMaxWaves * 16;                          // [waves][16]
-  float* a_buf = l_buf + kMaxWaves * 16;                          // [waves][16][128]
-  if (c == 0) {
-    m_buf[wave * 16 + n] = m_ref;
-    l_buf[wave * 16 + n] = l_tot;
+  float* m_buf = reinterpret_cast<float*>(lds);                   // [waves][8]
+  float* l_buf = m_buf + kMaxWaves * 8;                           // [waves][8]
+  float* a_buf = l_buf + kMaxWaves * 8;                           // [waves][8][128]
+  if (c == 0 && par == 0) {
+    m_buf[wave * 8 + hq] = m_ref;
+    l_buf[wave * 8 + hq] = l_tot;
   }
-  {
-    float* dst = a_buf + (wave * 16 + n) * kHeadDim + 32 * c;
+  if (par == 0) {
+    float* dst = a_buf + (wave * 8 + hq) * kHeadDim + 32 * c;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dst[8 * r + q] = acc[q][r];
+      for (int d = 0; d < 8; ++d) dst[8 * r + d] = o[r][d];
   }
   __syncthreads();
   if (st != 0 || !owner) return;
   float M = -__builtin_inff();
-  for (int t = 0; t < a.streams; ++t) M = fmaxf(M, m_buf[(t * a.heads_per_wg + gl) * 16 + n]);
+  for (int t = 0; t < a.streams; ++t) M = fmaxf(M, m_buf[(t * a.heads_per_wg + gl) * 8 + hq]);
   float lsum = 0.0f;
   float out[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) out[j] = 0.0f;
   for (int t = 0; t < a.streams; ++t) {
     const int wv = t * a.heads_per_wg + gl;
-    const float mt = m_buf[wv * 16 + n];
-    const float sc = (mt == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mt - M);
-    lsum += sc * l_buf[wv * 16 + n];
-    const float* src = a_buf + (wv * 16 + n) * kHeadDim + 32 * c;
+    const float mt = m_buf[wv * 8 + hq];
+    const float scl = (mt == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mt - M);
+    lsum += scl * l_buf[wv * 8 + hq];
+    const float* src = a_buf + (wv * 8 + hq) * kHeadDim + 32 * c;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) out[j] += sc * src[j];
+    for (int j = 0; j < 32; ++j) out[j] += scl * src[j];
   }
-  const int h = g * G + hq;
+  const int h = qh0 + hq;
   const int64_t slot = ((int64_t)b * a.num_q_heads + h) * S + s;
   const float inv = 1.0f / lsum;
   float* dst = a.part_acc + slot * kHeadDim + 32 * c;
 #pragma unroll
-  for (int j = 0; j < 32; j += 4) {
-    floatx4 v;
-    v.x = out[j] * inv; v.y = out[j + 1] * inv; v.z = out[j + 2] * inv; v.w = out[j + 3] * inv;
-    *reinterpret_cast<floatx4*>(dst + j) = v;
-  }
+  for (int j = 0; j < 32; j += 4)
+    *reinterpret_cast<floatx4*>(dst + j) = floatx4{out[j] * inv, out[j + 1] * inv, out[j + 2] * inv, out[j + 3] * inv};
   if (c == 0) a.part_lse[slot] = M + __builtin_log2f(lsum);
-}
-
-template <int KB, int VB, bool PACK>
-static hipError_t launch_decode_kvp(const DecodeArgs& a, int qt, hipStream_t st) {
-  const long long units = (long long)a.batch * a.head_groups * a.num_splits;
-  const dim3 grid((unsigned)units), block(64 * a.heads_per_wg * a.streams);
-  if (qt == 0)
-    hipLaunchKernelGGL((decode_split_kernel<KB, VB, 0, PACK>), grid, block, 0, st, a);
-  else if (qt == 1)
-    hipLaunchKernelGGL((decode_split_kernel<KB, VB, 1, PACK>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<KB, VB, 2, PACK>), grid, block, 0, st, a);
-  return hipGetLastError();
 }
 
 template <int KB, int VB>
 static hipError_t launch_decode_kv(const DecodeArgs& a, int qt, hipStream_t st) {
-  return a.group <= 8 ? launch_decode_kvp<KB, VB, true>(a, qt, st) : launch_decode_kvp<KB, VB, false>(a, qt, st);
+  const long long units = (long long)a.batch * a.head_groups * a.num_splits;
+  const dim3 grid((unsigned)units), block(64 * a.heads_per_wg * a.streams);
+  if (qt == 0)
+    hipLaunchKernelGGL((decode_split_kernel<KB, VB, 0>), grid, block, 0, st, a);
+  else if (qt == 1)
+    hipLaunchKernelGGL((decode_split_kernel<KB, VB, 1>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<KB, VB, 2>), grid, block, 0, st, a);
+  return hipGetLastError();
 }
 
 template <int KB>

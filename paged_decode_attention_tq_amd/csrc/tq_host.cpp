@@ -220,14 +220,17 @@ int device_cu_count() {
   return cache[dev];
 }
 
-// Decode work split.  A workgroup covers heads_per_wg KV heads (the largest
-// divisor of num_kv_heads up to 8) and pages_per_split pages of one sequence;
+// Decode work split.  A virtual head is a KV head with up to 8 of its query
+// heads (q_groups = ceil(group / 8) per KV head).  A workgroup covers
+// heads_per_wg virtual heads (the largest divisor of their count up to 8)
+// and pages_per_split pages of one sequence;
 // its waves are heads_per_wg x streams, streams = 8 / heads_per_wg page
 // streams per head.  The split count aims at one full round of two
 // workgroups per CU, keeps at least 8 splits for the longest sequence (so
 // ragged batches balance) and at most 64 splits (the merge holds one split
 // weight per lane).
 struct SplitPlan {
+  int q_groups;
   int heads_per_wg;
   int streams;
   int head_groups;
@@ -235,14 +238,16 @@ struct SplitPlan {
   int num_splits;
 };
 
-SplitPlan plan_split(int batch, int num_kv_heads, int max_seq_len, int num_cus) {
+SplitPlan plan_split(int batch, int num_kv_heads, int group, int max_seq_len, int num_cus) {
   SplitPlan p;
+  p.q_groups = (group + 7) / 8;
+  const int vheads = num_kv_heads * p.q_groups;
   p.heads_per_wg = 1;
   for (int h = 1; h <= 8; ++h)
-    if (num_kv_heads % h == 0) p.heads_per_wg = h;
+    if (vheads % h == 0) p.heads_per_wg = h;
   p.streams = 8 / p.heads_per_wg;
   if (p.streams < 1) p.streams = 1;
-  p.head_groups = num_kv_heads / p.heads_per_wg;
+  p.head_groups = vheads / p.heads_per_wg;
   const int max_pages = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
   if (max_pages <= 0) {
     p.pages_per_split = 1;
@@ -363,7 +368,7 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads, 
   (void)ctx;
   (void)block_size;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
-  SplitPlan p = plan_split(batch, num_kv_heads, max_seq_len, device_cu_count());
+  SplitPlan p = plan_split(batch, num_kv_heads, num_q_heads / num_kv_heads, max_seq_len, device_cu_count());
   size_t per = (size_t)batch * num_q_heads * p.num_splits;
   return per * (kHeadDim + 1) * sizeof(float) + 256;
 }
@@ -393,7 +398,7 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
       tq_decode_workspace_bytes(ctx, batch, num_q_heads, num_kv_heads, max_seq_len, block_size);
   if (!workspace || workspace_bytes < need) return TQ_ERR_WORKSPACE;
 
-  SplitPlan p = plan_split(batch, num_kv_heads, max_seq_len, device_cu_count());
+  SplitPlan p = plan_split(batch, num_kv_heads, group, max_seq_len, device_cu_count());
   const float sm_scale = scale > 0 ? scale : 1.0f / std::sqrt((float)kHeadDim);
   const float k_scale = ctx->tab_scale[k_bits];
   const float v_scale = ctx->tab_scale[v_bits];
@@ -415,6 +420,7 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   d.num_q_heads = num_q_heads;
   d.num_kv_heads = num_kv_heads;
   d.group = group;
+  d.q_groups = p.q_groups;
   d.max_blocks_per_seq = max_blocks_per_seq;
   d.heads_per_wg = p.heads_per_wg;
   d.streams = p.streams;

@@ -9,7 +9,7 @@ namespace tq {
 
 constexpr int kHeadDim = 128;    // the kernels are built for head_dim 128
 constexpr int kBlockSize = 16;   // decode page size (tokens per page)
-constexpr int kMaxGroup = 16;    // query heads per KV head handled by one wave
+constexpr int kMaxGroup = 64;    // query heads per KV head (groups of 8 per wave)
 
 // Arguments of the row-writer kernel (passed by value as kernel arguments).
 struct WriteArgs {
@@ -27,10 +27,11 @@ struct WriteArgs {
   float pos_bounds[16];     // the 2^(b-1) - 1 positive boundaries, increasing
 };
 
-// Arguments of the decode split kernel.  One workgroup handles one
-// (sequence, group of heads_per_wg KV heads, split) and runs
-// heads_per_wg * streams waves: each wave owns one KV head and every
-// streams-th page of the split, so the workgroup consumes whole pages.
+// Arguments of the decode split kernel.  A virtual head is one KV head with
+// up to 8 of its query heads.  One workgroup handles one (sequence, group of
+// heads_per_wg virtual heads, split) and runs heads_per_wg * streams waves:
+// each wave owns one virtual head and every streams-th page of the split,
+// so the workgroup consumes whole pages.
 struct DecodeArgs {
   const void* q;                 // [B, Hq, 128]
   const uint8_t* k_pages;
@@ -45,12 +46,13 @@ struct DecodeArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;                 // num_q_heads / num_kv_heads
+  int32_t q_groups;              // ceil(group / 8): query-head groups per KV head
   int32_t k_row_bytes;
   int32_t v_row_bytes;
   int32_t max_blocks_per_seq;
-  int32_t heads_per_wg;          // KV heads per workgroup (divides num_kv_heads)
+  int32_t heads_per_wg;          // virtual heads (KV head, query group) per workgroup
   int32_t streams;               // page streams per head in a workgroup
-  int32_t head_groups;           // num_kv_heads / heads_per_wg
+  int32_t head_groups;           // num_kv_heads * q_groups / heads_per_wg
   int32_t pages_per_split;       // pages per workgroup
   int32_t num_splits;            // S
   float q_scale;                 // softmax scale * log2(e) / (sqrt(128) * k_scale)

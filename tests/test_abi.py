@@ -61,8 +61,8 @@ def test_status_strings_and_argument_errors():
     assert lib.tq_write_kv(h, None, 9, 4, 2, None, 4, 16, None, 4, None, None) == 1  # bad dtype
     assert lib.tq_write_kv(h, None, 1, 0, 2, None, 4, 16, None, 4, None, None) == 0  # nothing to do
     p = ctypes.c_void_p(16)
-    args = dict(batch=2, hq=32, hkv=1)  # group 32 > 16
-    assert lib.tq_paged_decode(h, p, 1, 2, 32, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 2
+    args = dict(batch=2, hq=128, hkv=1)  # group 128 > 64
+    assert lib.tq_paged_decode(h, p, 1, 2, 128, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 2
     assert lib.tq_paged_decode(h, p, 1, 2, 6, 4, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 1
     assert lib.tq_paged_decode(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 32, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 2
     assert lib.tq_paged_decode(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 16, None) == 4
