@@ -40,9 +40,12 @@
 namespace tq {
 
 // ---------------------------------------------------------------------------
-// Replicated pair tables.  Row r of a b-bit table is at r << kShift; replica
-// k (k = lane & (kRep - 1)) of the hi pair at +4k, of the lo pair at
-// +kLoOff + 4k.
+// Replicated pair tables.  Row p = i0 | i1 << B holds, once per replica, the
+// 8-byte entry (hi, lo): hi = the fp16 pair (c[i0], c[i1]), lo = the fp16
+// pair of their rounding residuals.  Replica k = lane & (kRep - 1) sits at
+// (p << kShift) + 8k, so a half-wave's 8-byte reads hit distinct banks.
+// Keys read the whole entry; values read hi only (the centroids are scaled
+// so that fp16 holds them to about 1e-4 relative).
 template <int B>
 struct PairTable {
   static constexpr int kRows = 1 << (2 * B);
@@ -50,21 +53,19 @@ struct PairTable {
   static constexpr int kShift = (B == 5) ? 5 : 8;
   static constexpr int kStride = 1 << kShift;  // = 8 * kRep
   static constexpr int kBytes = kRows * kStride;
-  static constexpr int kLoOff = 4 * kRep;
 };
 
 template <int B>
-__device__ __forceinline__ void fill_pair_table(uint8_t* base, const float* cent) {
+__device__ __forceinline__ void fill_pair_table(uint8_t* base, const float* cent, int tid, int nthreads) {
   using T = PairTable<B>;
-  constexpr int kQuads = T::kBytes / 16;  // 4 replicas per 16-byte store
-  for (int i = threadIdx.x; i < kQuads; i += blockDim.x) {
-    const int word = 4 * i;
-    const int row = word / (2 * T::kRep);
-    const bool lo = (word % (2 * T::kRep)) >= T::kRep;
+  constexpr int kQuads = T::kBytes / 16;  // 2 replicas per 16-byte store
+  for (int i = tid; i < kQuads; i += nthreads) {
+    const int row = (2 * i) / T::kRep;
     const float c0 = cent[row & ((1 << B) - 1)], c1 = cent[row >> B];
     const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
-    const uint32_t v = lo ? pack_half2((_Float16)(c0 - (float)h0), (_Float16)(c1 - (float)h1)) : pack_half2(h0, h1);
-    *reinterpret_cast<u32x4*>(base + 4 * word) = u32x4{v, v, v, v};
+    const uint32_t hi = pack_half2(h0, h1);
+    const uint32_t lo = pack_half2((_Float16)(c0 - (float)h0), (_Float16)(c1 - (float)h1));
+    *reinterpret_cast<u32x4*>(base + 16 * i) = u32x4{hi, lo, hi, lo};
   }
 }
 
@@ -101,68 +102,187 @@ __device__ __forceinline__ float load_q(const void* q, int64_t i) {
   else return bf16_to_f32(static_cast<const uint16_t*>(q)[i]);
 }
 
+template <int R>
+__device__ __forceinline__ float quad_bcast(float v) {  // lane 4k + R of each quad to all four
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), R * 0x55, 0xF, 0xF, false));
+}
+
+// max over the four 16-lane rows (lanes n, n + 16, n + 32, n + 48)
+__device__ __forceinline__ float max_across_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ float row_ror8(float v) {  // lane n <-> n ^ 8 inside a 16-lane row
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ uint32_t ld_u32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
-__device__ __forceinline__ float ld_f32(const uint8_t* p) { return *reinterpret_cast<const float*>(p); }
+// ---------------------------------------------------------------------------
+// Page copies into LDS.  One buffer_load_dwordx4 with the lds modifier moves
+// 64 16-byte chunks (1 KB) from global memory straight into LDS at
+// M0 + 16 * lane, without passing through registers.  It is issued from
+// inline assembly so that the compiler does not treat the later LDS reads
+// of other slots as depending on it; the kernel waits for the copies itself
+// (s_waitcnt vmcnt) before the barrier that publishes a page.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// one page of one KV head, as loaded by one lane
-template <int KB, int VB>
-struct PageRegs {
-  uint32_t kw[KB];
-  float nk[4];
-  uint32_t vw[4];
-  uint32_t vw2[4];  // second word for 3- and 5-bit values
-  float nv[4];
-};
+__device__ __forceinline__ i32x4 buffer_rsrc(const uint8_t* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = (int)(uint32_t)p;
+  r.y = (int)((uint32_t)(p >> 32) & 0xFFFFu);
+  r.z = (int)bytes;
+  r.w = 0x00020000;
+  return r;
+}
 
-constexpr int kMaxWaves = 8;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy_chunk_to_lds(i32x4 rsrc, uint32_t lds_addr, uint32_t src_off) {
+  // both are uniform by construction; readfirstlane makes that visible
+  rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+  rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+  rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+  rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
+  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_addr), "v"(src_off), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n) (n clamped to 15, which only waits longer)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define TQ_VM(k) \
+  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | k); break;
+    TQ_VM(0) TQ_VM(1) TQ_VM(2) TQ_VM(3) TQ_VM(4) TQ_VM(5) TQ_VM(6) TQ_VM(7)
+    TQ_VM(8) TQ_VM(9) TQ_VM(10) TQ_VM(11) TQ_VM(12) TQ_VM(13) TQ_VM(14)
+#undef TQ_VM
+    default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15); break;
+  }
+}
+
+
+constexpr int kMaxWaves = 16;
 
 template <int KB, int VB, int QT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
+  // all of the CU's LDS, statically: addresses are then known constants
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kDecodeLdsBytes];
   using KT = PairTable<KB>;
   using VT = PairTable<VB>;
   constexpr bool kShareV = (KB == VB);
-  constexpr int kVBase = 0;
-  constexpr int kKBase = kShareV ? 0 : VT::kBytes;
-  constexpr int kTabBytes = kKBase + KT::kBytes;
-  constexpr int kMergeBytes = kMaxWaves * 8 * (kHeadDim + 2) * 4;
-  constexpr int kLds = kTabBytes > kMergeBytes ? kTabBytes : kMergeBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  // LDS: lookup tables at 0 (so their addresses need no base), then the
+  // page ring, then the split's block ids
+  constexpr int kVTab = 0;
+  constexpr int kKTab = kShareV ? 0 : VT::kBytes;
+  constexpr int kRing = kKTab + KT::kBytes;
 
   const int S = a.num_splits;
-  const int unit = blockIdx.x;
+  const int unit = __builtin_amdgcn_workgroup_id_x();
+  const int tid = __builtin_amdgcn_workitem_id_x();
   const int s = unit % S;
   const int hg = (unit / S) % a.head_groups;
   const int b = unit / (S * a.head_groups);
-  const int L = a.seq_lens[b];
+  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
   const int npages = (L + kBlockSize - 1) / kBlockSize;
   const int p0 = s * a.pages_per_split;
   if (p0 >= npages) return;  // the whole workgroup leaves together
-  const int p1 = min(p0 + a.pages_per_split, npages);
-
-  fill_pair_table<KB>(lds + kKBase, a.k_cent);
-  if constexpr (!kShareV) fill_pair_table<VB>(lds + kVBase, a.v_cent);
-  __syncthreads();
+  const int span = min(a.pages_per_split, npages - p0);
 
   // the wave index is uniform; say so, so that everything derived from it
-  // (head, page stream, page addresses) lives in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int gl = wave % a.heads_per_wg;
-  const int st = wave / a.heads_per_wg;
-  const int gv = hg * a.heads_per_wg + gl;     // virtual head: (KV head, group of <= 8 query heads)
-  const int g = gv / a.q_groups;               // KV head
-  const int qh0 = g * a.group + (gv % a.q_groups) * 8;
-  const int gsz = min(8, a.group - (gv % a.q_groups) * 8);  // query heads of this wave
+  // (head, page stream, copy assignment) lives in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int W = a.waves;
+  const int hpw = a.kv_per_wg * a.q_groups;    // waves per page
+  const int st = wave / hpw;                   // page stream
+  const int hs = wave - st * hpw;
+  const int kvl = hs / a.q_groups;
+  const int qgi = hs - kvl * a.q_groups;
+  const int g0 = hg * a.kv_per_wg;
+  const int g = g0 + kvl;                      // KV head
+  const int qh0 = g * a.group + qgi * 8;
+  const int gsz = min(8, a.group - qgi * 8);   // query heads of this wave
   const int n = lane & 15;
   const int c = lane >> 4;
   const int hq = n & 7;                        // query head (within the wave's group) of column n
   const int par = n >> 3;                      // column half: q_lo / odd value dims
-  const int span = p1 - p0;
-  const int nw = span > st ? (span - st + a.streams - 1) / a.streams : 0;
+  const int strm = a.streams;
+  const int R = a.ring_pages;
+
+  int32_t* bt_lds = reinterpret_cast<int32_t*>(lds + a.bt_base);  // the split's block ids
+  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)lds);
+
+  // ---- page copies ------------------------------------------------------------
+  // Page P of the split (0-based) lives in slot P % R.  Its copy is k_instr
+  // 1 KB loads of K rows then v_instr of V rows, issued by the hpw waves of
+  // stream P % strm (wave hs takes loads hs, hs + hpw, ...).  Window i of
+  // the copies is the pages strm*i + R - strm .. strm*i + R - 1, one per
+  // stream, so every window hands each wave the same loads of one page.
+  const int nK = a.k_instr;
+  const int nI = a.k_instr + a.v_instr;
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  const int my_off = R - strm + (((st - R) % strm) + strm) % strm;  // my page's offset in a window
+  const int rv0 = nK + (((hs - nK) % hpw) + hpw) % hpw;               // my first V load
+  const int n_my = (nI > hs) ? (nI - hs + hpw - 1) / hpw : 0;         // my loads per page
+  // my loads of the R - 2 strm pages that follow a multiple of strm
+  const int n_steady = n_my * ((R - 2 * strm > st) ? (R - 2 * strm - st + strm - 1) / strm : 0);
+  // per-token mode: lane source offset of chunk (ri * 64 + lane) of a region
+  auto token_chunk = [&](int ri, int C, int RB, float invC, uint32_t& off) {
+    // chunk k of token t: 16-byte aligned window over the token's slice
+    const int j = ri * 64 + lane;
+    const int t = (int)(((float)j + 0.5f) * invC);
+    const int k = j - t * C;
+    const int row0 = (t * a.num_kv_heads + g0) * RB;
+    off = (uint32_t)((row0 & ~15) + 16 * k);
+    return t < kBlockSize && (int)off < row0 + a.kv_per_wg * RB;
+  };
+  // window i; slot_i = (strm * i) % R
+  auto issue_window = [&](int i, int slot_i) {
+    const int P = strm * i + my_off;
+    if (P < 0 || P >= span) return;
+    int slot = slot_i + my_off;
+    if (slot >= R) slot -= R;
+    const int blk = __builtin_amdgcn_readfirstlane(bt_lds[P]);
+    const uint32_t dst0 = lds0 + (uint32_t)(kRing + slot * a.slot_bytes);
+    const i32x4 kr = buffer_rsrc(a.k_pages + (int64_t)blk * a.k_page_bytes, (uint32_t)a.k_page_bytes);
+    const i32x4 vr = buffer_rsrc(a.v_pages + (int64_t)blk * a.v_page_bytes, (uint32_t)a.v_page_bytes);
+    if (!a.per_token) {
+      // whole pages: chunk j of a region is bytes 16j .. 16j + 15
+#pragma unroll 1
+      for (int r = hs; r < nK; r += hpw) {
+        if (lane < a.k_chunks - r * 64) copy_chunk_to_lds(kr, dst0 + (uint32_t)(r * 1024), (uint32_t)(r * 1024) + lane16);
+      }
+      const uint32_t dv = dst0 + (uint32_t)a.k_region;
+#pragma unroll 1
+      for (int r = rv0 - nK; r < nI - nK; r += hpw) {
+        if (lane < a.v_chunks - r * 64) copy_chunk_to_lds(vr, dv + (uint32_t)(r * 1024), (uint32_t)(r * 1024) + lane16);
+      }
+    } else {
+#pragma unroll 1
+      for (int r = hs; r < nK; r += hpw) {
+        uint32_t off;
+        if (token_chunk(r, a.k_tok_chunks, a.k_row_bytes, a.k_inv_tok_chunks, off))
+          copy_chunk_to_lds(kr, dst0 + (uint32_t)(r * 1024), off);
+      }
+      const uint32_t dv = dst0 + (uint32_t)a.k_region;
+#pragma unroll 1
+      for (int r = rv0 - nK; r < nI - nK; r += hpw) {
+        uint32_t off;
+        if (token_chunk(r, a.v_tok_chunks, a.v_row_bytes, a.v_inv_tok_chunks, off))
+          copy_chunk_to_lds(vr, dv + (uint32_t)(r * 1024), off);
+      }
+    }
+  };
+  {
+    const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0;
+    for (int i = tid; i < span; i += 64 * W) bt_lds[i] = bt[i];
+  }
 
   // ---- rotated, scaled query as the B operand of the score MFMAs ----------
   // Lane (n, c) covers dims 32c..32c+31 (16 pairs); column n < 8 holds the
@@ -225,64 +345,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     }
   }
 
-  // ---- per-lane byte offsets inside a page --------------------------------
-  const int k_tok = a.num_kv_heads * a.k_row_bytes;  // bytes between tokens
-  const int v_tok = a.num_kv_heads * a.v_row_bytes;
-  const int k_idx_off = n * k_tok + g * a.k_row_bytes + 4 * KB * c;
-  const int k_norm_off = 4 * c * k_tok + g * a.k_row_bytes + a.k_row_bytes - 4;  // + r * k_tok
+  // every global load of the prologue has been consumed: the block ids are
+  // in LDS, the page copies can start (the compiler counts none of them)
+  __syncthreads();
+  // windows -m .. -1 cover pages 0 .. R - strm - 1
+  {
+    const int m = (R - strm + strm - 1) / strm;
+#pragma unroll 1
+    for (int i = -m; i < 0; ++i) issue_window(i, (((strm * i) % R) + R) % R);
+  }
+
+  // ---- lookup tables ----------------------------------------------------------
+  fill_pair_table<KB>(lds + kKTab, a.k_cent, tid, 64 * W);
+  if constexpr (!kShareV) fill_pair_table<VB>(lds + kVTab, a.v_cent, tid, 64 * W);
+
+  // ---- per-lane LDS offsets inside a page slot ----------------------------------
+  // token t of this wave's KV head starts at t * tstride + delta_t + kvl *
+  // row bytes in a slot.  delta_t, the 16-byte misalignment of the token's
+  // slice in per-token mode, is 4 * ((t * Hkv + g0) mod 4) since every row
+  // size is 4 mod 16.
+  auto delta = [&](int t) { return (((t * a.num_kv_heads + g0) & 3) << 2) & a.dmask; };
+  auto tok_k = [&](int t) { return t * a.k_tstride + delta(t) + kvl * a.k_row_bytes; };
+  auto tok_v = [&](int t) { return a.k_region + t * a.v_tstride + delta(t) + kvl * a.v_row_bytes; };
   const int v_byte = n * VB;
-  const int v_row = 4 * c * v_tok + g * a.v_row_bytes;                            // + j * v_tok
-  const int v_dat_off = v_row + ((VB == 3 || VB == 5) ? (v_byte & ~3) : (v_byte & ~1));
-  const int v_norm_off = v_row + a.v_row_bytes - 4;
+  const int v_dat = (VB == 3 || VB == 5) ? (v_byte & ~3) : (v_byte & ~1);
+  const uint32_t k_idx_off = (uint32_t)(kRing + tok_k(n) + 4 * KB * c);
+  // each lane reads the norms of token 4c + (n & 3); quad broadcasts hand
+  // every lane those of tokens 4c .. 4c + 3
+  const uint32_t k_norm_off = (uint32_t)(kRing + tok_k(4 * c + (n & 3)) + a.k_row_bytes - 4);
+  const uint32_t v_norm_off = (uint32_t)(kRing + tok_v(4 * c + (n & 3)) + a.v_row_bytes - 4);
+  uint32_t v_dat_off[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v_dat_off[r] = (uint32_t)(kRing + tok_v(4 * c + r) + v_dat);
   const uint32_t v_shift = 8u * (uint32_t)(v_byte & 3);
-  const uint32_t k_lane = (uint32_t)(lane & (KT::kRep - 1)) * 4u;
-  const uint32_t v_lane = (uint32_t)(lane & (VT::kRep - 1)) * 4u;
-  const uint8_t* k_tab = lds + kKBase;
-  const uint8_t* v_tab = kShareV ? (lds + kKBase) : (lds + kVBase);
+  const uint32_t k_lane = (uint32_t)(lane & (KT::kRep - 1)) * 8u;
+  const uint32_t v_lane = (uint32_t)(lane & (VT::kRep - 1)) * 8u;
+  const uint8_t* k_tab = lds + kKTab;
+  const uint8_t* v_tab = lds + kVTab;
   const uint32_t w_shift = 16u * (uint32_t)par;  // weight half: even dims in columns < 8
-
-  // ---- page walk ------------------------------------------------------------
-  const int32_t* __restrict__ bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0 + st;
-  const int strm = a.streams;
-  const int nwu = __builtin_amdgcn_readfirstlane(nw);
-  const int page_base = p0 + st;
-
-  // page data registers are refilled for the next page as soon as each part
-  // has been consumed, so one page of loads is always in flight
-  PageRegs<KB, VB> P;
-  __amdgpu_buffer_rsrc_t kr, vr;
-  auto set_page = [&](int blk_in) {
-    const int blk = __builtin_amdgcn_readfirstlane(blk_in);
-    kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.k_pages + (int64_t)blk * a.k_page_bytes),
-                                           (short)0, 0x7FFFFFFF, 0x00020000);
-    vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v_pages + (int64_t)blk * a.v_page_bytes),
-                                           (short)0, 0x7FFFFFFF, 0x00020000);
-  };
-  auto load_kw = [&]() {
-#pragma unroll
-    for (int i = 0; i < KB; ++i) P.kw[i] = __builtin_amdgcn_raw_buffer_load_b32(kr, k_idx_off, 4 * i, 0);
-  };
-  auto load_nk = [&]() {
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      P.nk[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(kr, k_norm_off, r * k_tok, 0));
-  };
-  auto load_vw = [&]() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (VB == 2) {
-        P.vw[j] = __builtin_amdgcn_raw_buffer_load_b16(vr, v_dat_off, j * v_tok, 0);
-      } else {
-        P.vw[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_dat_off, j * v_tok, 0);
-        if constexpr (VB == 3 || VB == 5) P.vw2[j] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_dat_off, j * v_tok + 4, 0);
-      }
-    }
-  };
-  auto load_nv = [&]() {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      P.nv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, v_norm_off, j * v_tok, 0));
-  };
 
   // acc[blk][r]: column n (head hq), dim 32c + 8r + 2blk + par
   floatx4 acc[4];
@@ -291,19 +391,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   float m_ref = -__builtin_inff();
   float l_part = 0.0f;
 
-  auto compute_page = [&](int i, auto full_tag, auto loads_tag) {
+  auto compute_page = [&](uint32_t pg, int tok0, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    constexpr bool more = decltype(loads_tag)::value;  // refill P for the next page
-    const int tok0 = (page_base + strm * i) * kBlockSize + 4 * c;
-    // -- key lookups: (hi, lo) fp16 pairs of 16 dim pairs, then refill
+    // pg: byte offset of the page slot from the ring start
+    uint32_t kw[KB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i) kw[i] = lds_u32(lds, pg + k_idx_off + 4 * i);
+    const float nk_mine = __uint_as_float(lds_u32(lds, pg + k_norm_off));
+    const float nv_mine = __uint_as_float(lds_u32(lds, pg + v_norm_off));
+    float nk[4], nv[4];
+    nk[0] = quad_bcast<0>(nk_mine);
+    nk[1] = quad_bcast<1>(nk_mine);
+    nk[2] = quad_bcast<2>(nk_mine);
+    nk[3] = quad_bcast<3>(nk_mine);
+    nv[0] = quad_bcast<0>(nv_mine);
+    nv[1] = quad_bcast<1>(nv_mine);
+    nv[2] = quad_bcast<2>(nv_mine);
+    nv[3] = quad_bcast<3>(nv_mine);
+    uint32_t vw[4], vw2[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (VB == 2) {
+        vw[r] = *reinterpret_cast<const uint16_t*>(lds + pg + v_dat_off[r]);
+      } else {
+        vw[r] = lds_u32(lds, pg + v_dat_off[r]);
+        if constexpr (VB == 3 || VB == 5) vw2[r] = lds_u32(lds, pg + v_dat_off[r] + 4);
+      }
+    }
     uint32_t kh[16], kl[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const uint32_t ad = pair_addr<KB>(P.kw, k, k_lane);
-      kh[k] = lds_u32(k_tab, ad);
-      kl[k] = lds_u32(k_tab + KT::kLoOff, ad);
+      const u32x2 e = *reinterpret_cast<const u32x2*>(k_tab + pair_addr<KB>(kw, k, k_lane));
+      kh[k] = e[0];
+      kl[k] = e[1];
     }
-    if constexpr (more) load_kw();
     // -- value lookups: dword (V[t][2p], V[t][2p+1]) for pair p = 4n + blk of
     // token 4c + j is exactly A[row n][k = 2j, 2j+1] of value block blk
     uint32_t va[4][4];
@@ -311,17 +432,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     for (int j = 0; j < 4; ++j) {
       uint32_t words[2];
       if constexpr (VB == 3 || VB == 5) {
-        const uint64_t all = ((((uint64_t)P.vw2[j]) << 32) | P.vw[j]) >> v_shift;
+        const uint64_t all = ((((uint64_t)vw2[j]) << 32) | vw[j]) >> v_shift;
         words[0] = (uint32_t)all;
         words[1] = (uint32_t)(all >> 32);
       } else {
-        words[0] = P.vw[j];
+        words[0] = vw[j];
         words[1] = 0;
       }
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) va[blk][j] = lds_u32(v_tab, pair_addr<VB>(words, blk, v_lane));
     }
-    if constexpr (more) load_vw();
     // -- scores: A = [K_hi(p), K_lo(p), K_hi(p'), K_lo(p')], B = [q(p), q(p), q(p'), q(p')]
     floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -335,15 +455,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     float full[4], xv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      full[r] = (sc[r] + row_ror8(sc[r])) * (P.nk[r] * q_unscale);
-      const float e = fmaxf(__builtin_fmaf((float)(__float_as_uint(P.nv[r]) >> 24), 2.0f, -126.0f), -64.0f);
+      full[r] = (sc[r] + row_ror8(sc[r])) * (nk[r] * q_unscale);
+      const float e = fmaxf(__builtin_fmaf((float)(__float_as_uint(nv[r]) >> 24), 2.0f, -126.0f), -64.0f);
       xv[r] = full[r] + e;
       if constexpr (!FULL) xv[r] = (tok0 + r < L) ? xv[r] : -__builtin_inff();
     }
-    if constexpr (more) load_nk();
     float pmax = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
-    pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
-    pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
+    pmax = max_across_rows(pmax);
     if (__builtin_amdgcn_ballot_w64(pmax > m_ref + 8.0f) != 0) {
       const float m_new = fmaxf(m_ref, pmax);
       const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -359,14 +477,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       float pr = __builtin_amdgcn_exp2f(full[r] - m_ref);
       if constexpr (!FULL) pr = (tok0 + r < L) ? pr : 0.0f;
       l_part += pr;
-      float wv = pr * P.nv[r];
+      float wv = pr * nv[r];
       if constexpr (!FULL) wv = (tok0 + r < L) ? wv : 0.0f;  // rows past the end may hold anything
       const _Float16 hi = (_Float16)wv;
       const _Float16 lo = (_Float16)(wv - (float)hi);
       whi[r] = (uint32_t)__builtin_bit_cast(uint16_t, hi) << w_shift;
       wlo[r] = (uint32_t)__builtin_bit_cast(uint16_t, lo) << w_shift;
     }
-    if constexpr (more) load_nv();
     const half8 Whi = __builtin_bit_cast(half8, u32x4{whi[0], whi[1], whi[2], whi[3]});
     const half8 Wlo = __builtin_bit_cast(half8, u32x4{wlo[0], wlo[1], wlo[2], wlo[3]});
     // -- values: acc[pair][col] += sum_(t, parity) V[t][2 pair + parity] * w[t][head] [parity == col half]
@@ -379,24 +496,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   };
 
   // ---- page loop ------------------------------------------------------------------
-  // Only a sequence's last page can be partial; it is peeled off so the loop
-  // body has a single path (no register copies of in-flight loads).
-  if (nwu > 0) {
-    const bool last_full = (page_base + strm * (nwu - 1) + 1) * kBlockSize <= L;
-    const int n_full = last_full ? nwu : nwu - 1;
-    set_page(bt[0]);
-    load_kw();
-    load_vw();
-    load_nk();
-    load_nv();
-    int id_next = bt[(int64_t)min(1, nwu - 1) * strm];
-    for (int i = 0; i < n_full; ++i) {
-      set_page(id_next);  // loads issued inside fetch page i + 1 (the last page again at the end)
-      id_next = bt[(int64_t)min(i + 2, nwu - 1) * strm];
-      compute_page(i, std::true_type{}, std::true_type{});
-    }
-    if (!last_full) compute_page(nwu - 1, std::false_type{}, std::false_type{});
-  }
+  // Iteration i computes pages strm*i .. strm*i + strm - 1 (one per stream).
+  // Before it: wait for this wave's copies of those pages, then a barrier
+  // (every wave's copies have landed and every wave is done with the slots
+  // of iteration i - 1), then the copies of the pages R - strm ahead go into
+  // the slots just freed.
+  const int nit = (span + strm - 1) / strm;
+  int my_slot = st;   // (strm * i + st) % R
+  int slot_i = 0;     // (strm * i) % R
+  auto iteration = [&](int i, auto full_tag) {
+    // pages < strm * (i + 1) must have landed; issued after them are, in the
+    // steady state, R - 2 strm whole pages, else wait for everything
+    wait_vmcnt(strm * i + R - strm <= span ? n_steady : 0);
+    __syncthreads();
+    issue_window(i, slot_i);
+    const int P = strm * i + st;
+    if (P < span) compute_page((uint32_t)(my_slot * a.slot_bytes), (p0 + P) * kBlockSize + 4 * c, full_tag);
+    my_slot += strm;
+    if (my_slot >= R) my_slot -= R;
+    slot_i += strm;
+    if (slot_i >= R) slot_i -= R;
+  };
+  // only the sequence's last page can be partial, and it is in the last
+  // iteration: the others skip the masking
+  for (int i = 0; i + 1 < nit; ++i) iteration(i, std::true_type{});
+  iteration(nit - 1, std::false_type{});
 
   // ---- finish the split ---------------------------------------------------------
   float l_tot = l_part + __shfl_xor(l_part, 16);
@@ -414,7 +538,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     }
   const bool owner = par == 0 && hq < gsz;
 
-  if (a.streams == 1) {
+  if (strm == 1) {
     if (owner) {
       const int h = qh0 + hq;
       const int64_t slot = ((int64_t)b * a.num_q_heads + h) * S + s;
@@ -430,7 +554,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     return;
   }
 
-  // several streams per head: merge them through LDS (the tables are dead)
+  // several streams per head: merge them through LDS (every copy has been
+  // waited for, so the ring and the tables are dead after the barrier)
   __syncthreads();
   float* m_buf = reinterpret_cast<float*>(lds);                   // [waves][8]
   float* l_buf = m_buf + kMaxWaves * 8;                           // [waves][8]
@@ -449,13 +574,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   __syncthreads();
   if (st != 0 || !owner) return;
   float M = -__builtin_inff();
-  for (int t = 0; t < a.streams; ++t) M = fmaxf(M, m_buf[(t * a.heads_per_wg + gl) * 8 + hq]);
+  for (int t = 0; t < strm; ++t) M = fmaxf(M, m_buf[(t * hpw + hs) * 8 + hq]);
   float lsum = 0.0f;
   float out[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) out[j] = 0.0f;
-  for (int t = 0; t < a.streams; ++t) {
-    const int wv = t * a.heads_per_wg + gl;
+  for (int t = 0; t < strm; ++t) {
+    const int wv = t * hpw + hs;
     const float mt = m_buf[wv * 8 + hq];
     const float scl = (mt == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mt - M);
     lsum += scl * l_buf[wv * 8 + hq];
@@ -473,37 +598,55 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   if (c == 0) a.part_lse[slot] = M + __builtin_log2f(lsum);
 }
 
-template <int KB, int VB>
-static hipError_t launch_decode_kv(const DecodeArgs& a, int qt, hipStream_t st) {
+int decode_table_bytes(int k_bits, int v_bits) {
+  auto bytes = [](int b) {
+    switch (b) {
+      case 2: return PairTable<2>::kBytes;
+      case 3: return PairTable<3>::kBytes;
+      case 4: return PairTable<4>::kBytes;
+      case 5: return PairTable<5>::kBytes;
+    }
+    return 0;
+  };
+  return k_bits == v_bits ? bytes(k_bits) : bytes(k_bits) + bytes(v_bits);
+}
+
+int decode_merge_lds_bytes() { return kMaxWaves * 8 * (kHeadDim + 2) * 4; }
+
+template <int KB, int VB, int QT>
+static hipError_t launch_decode_t(const DecodeArgs& a, size_t lds_bytes, hipStream_t st) {
+  (void)lds_bytes;  // the kernel holds the whole LDS statically
   const long long units = (long long)a.batch * a.head_groups * a.num_splits;
-  const dim3 grid((unsigned)units), block(64 * a.heads_per_wg * a.streams);
-  if (qt == 0)
-    hipLaunchKernelGGL((decode_split_kernel<KB, VB, 0>), grid, block, 0, st, a);
-  else if (qt == 1)
-    hipLaunchKernelGGL((decode_split_kernel<KB, VB, 1>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<KB, VB, 2>), grid, block, 0, st, a);
+  hipLaunchKernelGGL((decode_split_kernel<KB, VB, QT>), dim3((unsigned)units), dim3(64 * a.waves), 0, st, a);
   return hipGetLastError();
 }
 
+template <int KB, int VB>
+static hipError_t launch_decode_kv(const DecodeArgs& a, int qt, size_t lds, hipStream_t st) {
+  if (qt == 0) return launch_decode_t<KB, VB, 0>(a, lds, st);
+  if (qt == 1) return launch_decode_t<KB, VB, 1>(a, lds, st);
+  return launch_decode_t<KB, VB, 2>(a, lds, st);
+}
+
 template <int KB>
-static hipError_t launch_decode_k(const DecodeArgs& a, int qt, int vb, hipStream_t st) {
+static hipError_t launch_decode_k(const DecodeArgs& a, int qt, int vb, size_t lds, hipStream_t st) {
   switch (vb) {
-    case 2: return launch_decode_kv<KB, 2>(a, qt, st);
-    case 3: return launch_decode_kv<KB, 3>(a, qt, st);
-    case 4: return launch_decode_kv<KB, 4>(a, qt, st);
-    case 5: return launch_decode_kv<KB, 5>(a, qt, st);
+    case 2: return launch_decode_kv<KB, 2>(a, qt, lds, st);
+    case 3: return launch_decode_kv<KB, 3>(a, qt, lds, st);
+    case 4: return launch_decode_kv<KB, 4>(a, qt, lds, st);
+    case 5: return launch_decode_kv<KB, 5>(a, qt, lds, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, size_t lds_bytes,
+                         hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   switch (k_bits) {
-    case 2: return launch_decode_k<2>(a, q_dtype, v_bits, stream);
-    case 3: return launch_decode_k<3>(a, q_dtype, v_bits, stream);
-    case 4: return launch_decode_k<4>(a, q_dtype, v_bits, stream);
-    case 5: return launch_decode_k<5>(a, q_dtype, v_bits, stream);
+    case 2: return launch_decode_k<2>(a, q_dtype, v_bits, lds_bytes, stream);
+    case 3: return launch_decode_k<3>(a, q_dtype, v_bits, lds_bytes, stream);
+    case 4: return launch_decode_k<4>(a, q_dtype, v_bits, lds_bytes, stream);
+    case 5: return launch_decode_k<5>(a, q_dtype, v_bits, lds_bytes, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -515,8 +658,9 @@ hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bit
 // l + 64; lane s holds the weight of split s (at most 64 splits).
 // ===========================================================================
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int tid = __builtin_amdgcn_workitem_id_x();
+  const int lane = tid & 63;
+  const int unit = __builtin_amdgcn_workgroup_id_x() * 4 + (tid >> 6);
   if (unit >= a.batch * a.num_q_heads) return;
   const int b = unit / a.num_q_heads;
   const int L = a.seq_lens[b];

@@ -9,6 +9,7 @@ namespace tq {
 
 constexpr int kHeadDim = 128;    // the kernels are built for head_dim 128
 constexpr int kBlockSize = 16;   // decode page size (tokens per page)
+constexpr int kDecodeLdsBytes = 160 * 1024;  // LDS of one gfx950 CU, all of it used by the decode
 constexpr int kMaxGroup = 64;    // query heads per KV head (groups of 8 per wave)
 
 // Arguments of the row-writer kernel (passed by value as kernel arguments).
@@ -27,11 +28,12 @@ struct WriteArgs {
   float pos_bounds[16];     // the 2^(b-1) - 1 positive boundaries, increasing
 };
 
-// Arguments of the decode split kernel.  A virtual head is one KV head with
-// up to 8 of its query heads.  One workgroup handles one (sequence, group of
-// heads_per_wg virtual heads, split) and runs heads_per_wg * streams waves:
-// each wave owns one virtual head and every streams-th page of the split,
-// so the workgroup consumes whole pages.
+// Arguments of the decode split kernel.  One workgroup handles one
+// (sequence, group of kv_per_wg KV heads, split of pages_per_split pages).
+// It copies the pages' rows of its KV heads into a ring of LDS page slots
+// and runs waves = kv_per_wg * q_groups * streams waves: each wave owns one
+// KV head, one group of up to 8 of its query heads, and every streams-th
+// page of the split.
 struct DecodeArgs {
   const void* q;                 // [B, Hq, 128]
   const uint8_t* k_pages;
@@ -46,15 +48,29 @@ struct DecodeArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;                 // num_q_heads / num_kv_heads
-  int32_t q_groups;              // ceil(group / 8): query-head groups per KV head
+  int32_t q_groups;              // ceil(group / 8)
   int32_t k_row_bytes;
   int32_t v_row_bytes;
   int32_t max_blocks_per_seq;
-  int32_t heads_per_wg;          // virtual heads (KV head, query group) per workgroup
-  int32_t streams;               // page streams per head in a workgroup
-  int32_t head_groups;           // num_kv_heads * q_groups / heads_per_wg
+  int32_t kv_per_wg;             // KV heads of one workgroup
+  int32_t head_groups;           // num_kv_heads / kv_per_wg
+  int32_t streams;               // pages computed per iteration
+  int32_t waves;                 // kv_per_wg * q_groups * streams (<= 16)
   int32_t pages_per_split;       // pages per workgroup
   int32_t num_splits;            // S
+  int32_t ring_pages;            // LDS page slots (> streams)
+  int32_t slot_bytes;            // k_region + v_region
+  int32_t bt_base;               // LDS byte offset of the split's block ids
+  int32_t per_token;             // 0: whole page copied (kv_per_wg == num_kv_heads)
+                                 // 1: per-token slices of the workgroup's heads
+  int32_t dmask;                 // 15 in per-token mode, else 0
+  // per component (K, V):
+  int32_t k_region, v_region;    // LDS bytes of one page's staged rows
+  int32_t k_chunks, v_chunks;    // 16-byte chunks copied per page
+  int32_t k_instr, v_instr;      // ceil(chunks / 64): 1 KB copies per page
+  int32_t k_tok_chunks, v_tok_chunks;  // per-token mode: chunks per token
+  int32_t k_tstride, v_tstride;  // LDS bytes between consecutive tokens
+  float k_inv_tok_chunks, v_inv_tok_chunks;
   float q_scale;                 // softmax scale * log2(e) / (sqrt(128) * k_scale)
   uint32_t sign_bits[kHeadDim / 32];
   float k_cent[32];              // fp32 centroids of K times k_scale
@@ -76,7 +92,10 @@ struct MergeArgs {
 };
 
 hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, size_t lds_bytes,
+                         hipStream_t stream);
+int decode_table_bytes(int k_bits, int v_bits);  // LDS bytes of the decode lookup tables
+int decode_merge_lds_bytes();                     // LDS bytes of the stream merge
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace tq

@@ -81,6 +81,15 @@ def test_group_sizes(ctx, G):
     _run(ctx, w)
 
 
+@pytest.mark.parametrize("hkv,G,kb,vb", [(32, 1, 4, 4), (4, 40, 4, 2), (6, 24, 3, 5), (16, 1, 2, 3)])
+def test_kv_head_slices(ctx, hkv, G, kb, vb):
+    # more KV heads x query groups than one workgroup holds: each workgroup
+    # stages per-token slices of its heads (including 4- and 8-byte misalignments)
+    w = workloads.make_workload(f"slices{hkv}x{G}", k_bits=kb, v_bits=vb, num_q_heads=hkv * G, num_kv_heads=hkv,
+                                seq_lens=[130, 47, 300], seed=hkv + G)
+    _run(ctx, w)
+
+
 def test_many_splits_and_ragged_tails(ctx):
     # long enough for many 16-page splits per sequence, with ragged last pages
     w = workloads.make_workload("splits", num_q_heads=8, num_kv_heads=1, seq_lens=[9000, 4097, 255, 16, 15],
