@@ -40,12 +40,15 @@
 namespace tq {
 
 // ---------------------------------------------------------------------------
-// Replicated pair tables.  Row p = i0 | i1 << B holds, once per replica, the
-// 8-byte entry (hi, lo): hi = the fp16 pair (c[i0], c[i1]), lo = the fp16
-// pair of their rounding residuals.  Replica k = lane & (kRep - 1) sits at
-// (p << kShift) + 8k, so a half-wave's 8-byte reads hit distinct banks.
-// Keys read the whole entry; values read hi only (the centroids are scaled
-// so that fp16 holds them to about 1e-4 relative).
+// Replicated pair tables.  Row p = i0 | i1 << B holds, once per replica, an
+// 8-byte entry of two dwords: hi = the fp16 pair (c[i0], c[i1]) and lo = the
+// fp16 pair of their rounding residuals.  Replica k = lane & (kRep - 1) sits
+// at (p << kShift) + 8k, so a half-wave's 8-byte reads hit distinct banks.
+// Keys read the whole entry (the score MFMA multiplies both dwords by the
+// same query pair, so their order does not matter); values read hi only
+// (the centroids are scaled so that fp16 holds them to about 1e-4
+// relative).  The upper half of the replicas stores (lo, hi), which puts
+// the hi dwords of a half-wave on distinct banks too.
 template <int B>
 struct PairTable {
   static constexpr int kRows = 1 << (2 * B);
@@ -65,7 +68,8 @@ __device__ __forceinline__ void fill_pair_table(uint8_t* base, const float* cent
     const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
     const uint32_t hi = pack_half2(h0, h1);
     const uint32_t lo = pack_half2((_Float16)(c0 - (float)h0), (_Float16)(c1 - (float)h1));
-    *reinterpret_cast<u32x4*>(base + 16 * i) = u32x4{hi, lo, hi, lo};
+    const bool swap = ((2 * i) % T::kRep) >= T::kRep / 2;
+    *reinterpret_cast<u32x4*>(base + 16 * i) = swap ? u32x4{lo, hi, lo, hi} : u32x4{hi, lo, hi, lo};
   }
 }
 
@@ -154,18 +158,30 @@ __device__ __forceinline__ void copy_chunk_to_lds(i32x4 rsrc, uint32_t lds_addr,
 }
 #pragma clang diagnostic pop
 
-// s_waitcnt vmcnt(n) (n clamped to 15, which only waits longer)
+// s_waitcnt vmcnt(n) (n clamped to 15, which only waits longer).  Written
+// as assembly with a memory clobber so that no LDS read of the page being
+// waited for is scheduled above it.
 __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
 #define TQ_VM(k) \
-  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | k); break;
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
     TQ_VM(0) TQ_VM(1) TQ_VM(2) TQ_VM(3) TQ_VM(4) TQ_VM(5) TQ_VM(6) TQ_VM(7)
     TQ_VM(8) TQ_VM(9) TQ_VM(10) TQ_VM(11) TQ_VM(12) TQ_VM(13) TQ_VM(14)
 #undef TQ_VM
-    default: __builtin_amdgcn_s_waitcnt(0x0F70 | 15); break;
+    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
   }
 }
 
+// A row of a b-bit component in LDS: the 16-byte chunks of the window that
+// covers it (at most 12 bytes before its start), C of them per token.
+template <int B>
+struct RowWindow {
+  static constexpr int kRowBytes = (kHeadDim * B + 7) / 8 + 4;
+  static constexpr int kChunks = (kRowBytes + 12 + 15) / 16;
+  static constexpr int kPageBytes = kBlockSize * 16 * kChunks;           // one page of one head
+  static constexpr int kLoads = (kBlockSize * kChunks + 63) / 64;        // 1 KB loads per page
+  static constexpr int kLastLanes = kBlockSize * kChunks - 64 * (kLoads - 1);
+};
 
 constexpr int kMaxWaves = 16;
 
@@ -175,12 +191,15 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDecodeLdsBytes];
   using KT = PairTable<KB>;
   using VT = PairTable<VB>;
+  using KS = RowWindow<KB>;
+  using VS = RowWindow<VB>;
   constexpr bool kShareV = (KB == VB);
-  // LDS: lookup tables at 0 (so their addresses need no base), then the
-  // page ring, then the split's block ids
+  // LDS: lookup tables at 0 (so their addresses need no base), then one
+  // two-slot ring per wave
   constexpr int kVTab = 0;
   constexpr int kKTab = kShareV ? 0 : VT::kBytes;
   constexpr int kRing = kKTab + KT::kBytes;
+  constexpr int kSlot = KS::kPageBytes + VS::kPageBytes;  // one page of one KV head
 
   const int S = a.num_splits;
   const int unit = __builtin_amdgcn_workgroup_id_x();
@@ -195,7 +214,7 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   const int span = min(a.pages_per_split, npages - p0);
 
   // the wave index is uniform; say so, so that everything derived from it
-  // (head, page stream, copy assignment) lives in scalar registers
+  // (head, page stream, ring) lives in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int W = a.waves;
@@ -204,8 +223,7 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   const int hs = wave - st * hpw;
   const int kvl = hs / a.q_groups;
   const int qgi = hs - kvl * a.q_groups;
-  const int g0 = hg * a.kv_per_wg;
-  const int g = g0 + kvl;                      // KV head
+  const int g = hg * a.kv_per_wg + kvl;        // KV head
   const int qh0 = g * a.group + qgi * 8;
   const int gsz = min(8, a.group - qgi * 8);   // query heads of this wave
   const int n = lane & 15;
@@ -213,76 +231,56 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   const int hq = n & 7;                        // query head (within the wave's group) of column n
   const int par = n >> 3;                      // column half: q_lo / odd value dims
   const int strm = a.streams;
-  const int R = a.ring_pages;
+  // this wave's pages: st, st + strm, ... of the split
+  const int n_my = span > st ? (span - st + strm - 1) / strm : 0;
 
-  int32_t* bt_lds = reinterpret_cast<int32_t*>(lds + a.bt_base);  // the split's block ids
   const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)lds);
 
   // ---- page copies ------------------------------------------------------------
-  // Page P of the split (0-based) lives in slot P % R.  Its copy is k_instr
-  // 1 KB loads of K rows then v_instr of V rows, issued by the hpw waves of
-  // stream P % strm (wave hs takes loads hs, hs + hpw, ...).  Window i of
-  // the copies is the pages strm*i + R - strm .. strm*i + R - 1, one per
-  // stream, so every window hands each wave the same loads of one page.
-  const int nK = a.k_instr;
-  const int nI = a.k_instr + a.v_instr;
-  const uint32_t lane16 = 16u * (uint32_t)lane;
-  const int my_off = R - strm + (((st - R) % strm) + strm) % strm;  // my page's offset in a window
-  const int rv0 = nK + (((hs - nK) % hpw) + hpw) % hpw;               // my first V load
-  const int n_my = (nI > hs) ? (nI - hs + hpw - 1) / hpw : 0;         // my loads per page
-  // my loads of the R - 2 strm pages that follow a multiple of strm
-  const int n_steady = n_my * ((R - 2 * strm > st) ? (R - 2 * strm - st + strm - 1) / strm : 0);
-  // per-token mode: lane source offset of chunk (ri * 64 + lane) of a region
-  auto token_chunk = [&](int ri, int C, int RB, float invC, uint32_t& off) {
-    // chunk k of token t: 16-byte aligned window over the token's slice
-    const int j = ri * 64 + lane;
-    const int t = (int)(((float)j + 0.5f) * invC);
-    const int k = j - t * C;
-    const int row0 = (t * a.num_kv_heads + g0) * RB;
-    off = (uint32_t)((row0 & ~15) + 16 * k);
-    return t < kBlockSize && (int)off < row0 + a.kv_per_wg * RB;
+  // Each wave copies the rows of its own KV head, and only those, into its
+  // own two LDS slots: K then V, token t at t * 16C + delta_t, where the
+  // 16-byte window of C chunks covering the row starts delta_t bytes before
+  // it.  No other wave reads them, so the wave only waits for its own loads.
+  const uint32_t ring = (uint32_t)(kRing + wave * 2 * kSlot);
+  const int k_rows = (int)a.k_page_bytes, v_rows = (int)a.v_page_bytes;
+  // window start and row start of token t in a page
+  auto window = [&](int t, int RB, int C, int page_bytes, int& delta) {
+    const int row = (t * a.num_kv_heads + g) * RB;
+    int w = row & ~15;
+    if (w + 16 * C > page_bytes) w = page_bytes - 16 * C;
+    delta = row - w;
+    return w;
   };
-  // window i; slot_i = (strm * i) % R
-  auto issue_window = [&](int i, int slot_i) {
-    const int P = strm * i + my_off;
-    if (P < 0 || P >= span) return;
-    int slot = slot_i + my_off;
-    if (slot >= R) slot -= R;
-    const int blk = __builtin_amdgcn_readfirstlane(bt_lds[P]);
-    const uint32_t dst0 = lds0 + (uint32_t)(kRing + slot * a.slot_bytes);
-    const i32x4 kr = buffer_rsrc(a.k_pages + (int64_t)blk * a.k_page_bytes, (uint32_t)a.k_page_bytes);
-    const i32x4 vr = buffer_rsrc(a.v_pages + (int64_t)blk * a.v_page_bytes, (uint32_t)a.v_page_bytes);
-    if (!a.per_token) {
-      // whole pages: chunk j of a region is bytes 16j .. 16j + 15
-#pragma unroll 1
-      for (int r = hs; r < nK; r += hpw) {
-        if (lane < a.k_chunks - r * 64) copy_chunk_to_lds(kr, dst0 + (uint32_t)(r * 1024), (uint32_t)(r * 1024) + lane16);
-      }
-      const uint32_t dv = dst0 + (uint32_t)a.k_region;
-#pragma unroll 1
-      for (int r = rv0 - nK; r < nI - nK; r += hpw) {
-        if (lane < a.v_chunks - r * 64) copy_chunk_to_lds(vr, dv + (uint32_t)(r * 1024), (uint32_t)(r * 1024) + lane16);
-      }
+  // per-lane source offsets of the (at most two) 1 KB loads per component
+  uint32_t k_src[2], v_src[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    int d;
+    const int jk = 64 * q + lane, tk = jk / KS::kChunks;
+    k_src[q] = (uint32_t)(window(min(tk, kBlockSize - 1), a.k_row_bytes, KS::kChunks, k_rows, d) + 16 * (jk - tk * KS::kChunks));
+    if constexpr (KB == VB) {
+      v_src[q] = k_src[q];  // same row size, same page size: same windows
     } else {
-#pragma unroll 1
-      for (int r = hs; r < nK; r += hpw) {
-        uint32_t off;
-        if (token_chunk(r, a.k_tok_chunks, a.k_row_bytes, a.k_inv_tok_chunks, off))
-          copy_chunk_to_lds(kr, dst0 + (uint32_t)(r * 1024), off);
-      }
-      const uint32_t dv = dst0 + (uint32_t)a.k_region;
-#pragma unroll 1
-      for (int r = rv0 - nK; r < nI - nK; r += hpw) {
-        uint32_t off;
-        if (token_chunk(r, a.v_tok_chunks, a.v_row_bytes, a.v_inv_tok_chunks, off))
-          copy_chunk_to_lds(vr, dv + (uint32_t)(r * 1024), off);
-      }
+      const int jv = 64 * q + lane, tv = jv / VS::kChunks;
+      v_src[q] = (uint32_t)(window(min(tv, kBlockSize - 1), a.v_row_bytes, VS::kChunks, v_rows, d) + 16 * (jv - tv * VS::kChunks));
     }
-  };
-  {
-    const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0;
-    for (int i = tid; i < span; i += 64 * W) bt_lds[i] = bt[i];
   }
+  // the split's block ids are staged in LDS after the rings
+  const int32_t* bt_lds = reinterpret_cast<const int32_t*>(lds + kRing + W * 2 * kSlot);
+  auto issue_page = [&](int i) {  // this wave's page i into slot i & 1
+    const int blk = __builtin_amdgcn_readfirstlane(bt_lds[st + strm * i]);
+    const uint32_t dst = lds0 + ring + (uint32_t)((i & 1) * kSlot);
+    const i32x4 kr = buffer_rsrc(a.k_pages + (int64_t)blk * a.k_page_bytes, (uint32_t)k_rows);
+#pragma unroll
+    for (int q = 0; q < KS::kLoads; ++q)
+      if (q + 1 < KS::kLoads || lane < KS::kLastLanes) copy_chunk_to_lds(kr, dst + 1024u * q, k_src[q]);
+    const i32x4 vr = buffer_rsrc(a.v_pages + (int64_t)blk * a.v_page_bytes, (uint32_t)v_rows);
+#pragma unroll
+    for (int q = 0; q < VS::kLoads; ++q)
+      if (q + 1 < VS::kLoads || lane < VS::kLastLanes)
+        copy_chunk_to_lds(vr, dst + (uint32_t)KS::kPageBytes + 1024u * q, v_src[q]);
+  };
+  constexpr int kLoadsPerPage = KS::kLoads + VS::kLoads;
 
   // ---- rotated, scaled query as the B operand of the score MFMAs ----------
   // Lane (n, c) covers dims 32c..32c+31 (16 pairs); column n < 8 holds the
@@ -345,41 +343,41 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  // every global load of the prologue has been consumed: the block ids are
-  // in LDS, the page copies can start (the compiler counts none of them)
-  __syncthreads();
-  // windows -m .. -1 cover pages 0 .. R - strm - 1
-  {
-    const int m = (R - strm + strm - 1) / strm;
-#pragma unroll 1
-    for (int i = -m; i < 0; ++i) issue_window(i, (((strm * i) % R) + R) % R);
-  }
-
-  // ---- lookup tables ----------------------------------------------------------
+  // ---- lookup tables and block ids -------------------------------------------
   fill_pair_table<KB>(lds + kKTab, a.k_cent, tid, 64 * W);
   if constexpr (!kShareV) fill_pair_table<VB>(lds + kVTab, a.v_cent, tid, 64 * W);
+  {
+    const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0;
+    int32_t* dst = reinterpret_cast<int32_t*>(lds + kRing + W * 2 * kSlot);
+    for (int i = tid; i < span; i += 64 * W) dst[i] = bt[i];
+  }
+  __syncthreads();
 
-  // ---- per-lane LDS offsets inside a page slot ----------------------------------
-  // token t of this wave's KV head starts at t * tstride + delta_t + kvl *
-  // row bytes in a slot.  delta_t, the 16-byte misalignment of the token's
-  // slice in per-token mode, is 4 * ((t * Hkv + g0) mod 4) since every row
-  // size is 4 mod 16.
-  auto delta = [&](int t) { return (((t * a.num_kv_heads + g0) & 3) << 2) & a.dmask; };
-  auto tok_k = [&](int t) { return t * a.k_tstride + delta(t) + kvl * a.k_row_bytes; };
-  auto tok_v = [&](int t) { return a.k_region + t * a.v_tstride + delta(t) + kvl * a.v_row_bytes; };
+  // ---- per-lane LDS offsets inside a slot ---------------------------------------
+  auto tok_k = [&](int t) {
+    int d;
+    (void)window(t, a.k_row_bytes, KS::kChunks, k_rows, d);
+    return (int)ring + t * 16 * KS::kChunks + d;
+  };
+  auto tok_v = [&](int t) {
+    int d;
+    (void)window(t, a.v_row_bytes, VS::kChunks, v_rows, d);
+    return (int)ring + KS::kPageBytes + t * 16 * VS::kChunks + d;
+  };
   const int v_byte = n * VB;
   const int v_dat = (VB == 3 || VB == 5) ? (v_byte & ~3) : (v_byte & ~1);
-  const uint32_t k_idx_off = (uint32_t)(kRing + tok_k(n) + 4 * KB * c);
+  const uint32_t k_idx_off = (uint32_t)(tok_k(n) + 4 * KB * c);
   // each lane reads the norms of token 4c + (n & 3); quad broadcasts hand
   // every lane those of tokens 4c .. 4c + 3
-  const uint32_t k_norm_off = (uint32_t)(kRing + tok_k(4 * c + (n & 3)) + a.k_row_bytes - 4);
-  const uint32_t v_norm_off = (uint32_t)(kRing + tok_v(4 * c + (n & 3)) + a.v_row_bytes - 4);
+  const uint32_t k_norm_off = (uint32_t)(tok_k(4 * c + (n & 3)) + a.k_row_bytes - 4);
+  const uint32_t v_norm_off = (uint32_t)(tok_v(4 * c + (n & 3)) + a.v_row_bytes - 4);
   uint32_t v_dat_off[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v_dat_off[r] = (uint32_t)(kRing + tok_v(4 * c + r) + v_dat);
+  for (int r = 0; r < 4; ++r) v_dat_off[r] = (uint32_t)(tok_v(4 * c + r) + v_dat);
   const uint32_t v_shift = 8u * (uint32_t)(v_byte & 3);
   const uint32_t k_lane = (uint32_t)(lane & (KT::kRep - 1)) * 8u;
-  const uint32_t v_lane = (uint32_t)(lane & (VT::kRep - 1)) * 8u;
+  // the hi dword of this lane's replica
+  const uint32_t v_lane = (uint32_t)(lane & (VT::kRep - 1)) * 8u + (((lane & (VT::kRep - 1)) >= VT::kRep / 2) ? 4u : 0u);
   const uint8_t* k_tab = lds + kKTab;
   const uint8_t* v_tab = lds + kVTab;
   const uint32_t w_shift = 16u * (uint32_t)par;  // weight half: even dims in columns < 8
@@ -496,31 +494,26 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   };
 
   // ---- page loop ------------------------------------------------------------------
-  // Iteration i computes pages strm*i .. strm*i + strm - 1 (one per stream).
-  // Before it: wait for this wave's copies of those pages, then a barrier
-  // (every wave's copies have landed and every wave is done with the slots
-  // of iteration i - 1), then the copies of the pages R - strm ahead go into
-  // the slots just freed.
-  const int nit = (span + strm - 1) / strm;
-  int my_slot = st;   // (strm * i + st) % R
-  int slot_i = 0;     // (strm * i) % R
+  // Page i + 1 is copied while page i is computed.  The loads of a page are
+  // this wave's only memory operations in the loop, so "page i has landed"
+  // is "at most kLoadsPerPage loads outstanding".
   auto iteration = [&](int i, auto full_tag) {
-    // pages < strm * (i + 1) must have landed; issued after them are, in the
-    // steady state, R - 2 strm whole pages, else wait for everything
-    wait_vmcnt(strm * i + R - strm <= span ? n_steady : 0);
-    __syncthreads();
-    issue_window(i, slot_i);
-    const int P = strm * i + st;
-    if (P < span) compute_page((uint32_t)(my_slot * a.slot_bytes), (p0 + P) * kBlockSize + 4 * c, full_tag);
-    my_slot += strm;
-    if (my_slot >= R) my_slot -= R;
-    slot_i += strm;
-    if (slot_i >= R) slot_i -= R;
+    if (i + 1 < n_my) {
+      issue_page(i + 1);
+      wait_vmcnt(kLoadsPerPage);
+    } else {
+      wait_vmcnt(0);
+    }
+    const int P = st + strm * i;
+    compute_page((uint32_t)((i & 1) * kSlot), (p0 + P) * kBlockSize + 4 * c, full_tag);
   };
-  // only the sequence's last page can be partial, and it is in the last
-  // iteration: the others skip the masking
-  for (int i = 0; i + 1 < nit; ++i) iteration(i, std::true_type{});
-  iteration(nit - 1, std::false_type{});
+  if (n_my > 0) {
+    issue_page(0);
+    // only the sequence's last page can be partial, and it is this wave's
+    // last page if this wave has it
+    for (int i = 0; i + 1 < n_my; ++i) iteration(i, std::true_type{});
+    iteration(n_my - 1, std::false_type{});
+  }
 
   // ---- finish the split ---------------------------------------------------------
   float l_tot = l_part + __shfl_xor(l_part, 16);
@@ -555,7 +548,7 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   }
 
   // several streams per head: merge them through LDS (every copy has been
-  // waited for, so the ring and the tables are dead after the barrier)
+  // waited for, so the rings and the tables are dead after the barrier)
   __syncthreads();
   float* m_buf = reinterpret_cast<float*>(lds);                   // [waves][8]
   float* l_buf = m_buf + kMaxWaves * 8;                           // [waves][8]
@@ -614,39 +607,37 @@ int decode_table_bytes(int k_bits, int v_bits) {
 int decode_merge_lds_bytes() { return kMaxWaves * 8 * (kHeadDim + 2) * 4; }
 
 template <int KB, int VB, int QT>
-static hipError_t launch_decode_t(const DecodeArgs& a, size_t lds_bytes, hipStream_t st) {
-  (void)lds_bytes;  // the kernel holds the whole LDS statically
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const long long units = (long long)a.batch * a.head_groups * a.num_splits;
   hipLaunchKernelGGL((decode_split_kernel<KB, VB, QT>), dim3((unsigned)units), dim3(64 * a.waves), 0, st, a);
   return hipGetLastError();
 }
 
 template <int KB, int VB>
-static hipError_t launch_decode_kv(const DecodeArgs& a, int qt, size_t lds, hipStream_t st) {
-  if (qt == 0) return launch_decode_t<KB, VB, 0>(a, lds, st);
-  if (qt == 1) return launch_decode_t<KB, VB, 1>(a, lds, st);
-  return launch_decode_t<KB, VB, 2>(a, lds, st);
+static hipError_t launch_decode_kv(const DecodeArgs& a, int qt, hipStream_t st) {
+  if (qt == 0) return launch_decode_t<KB, VB, 0>(a, st);
+  if (qt == 1) return launch_decode_t<KB, VB, 1>(a, st);
+  return launch_decode_t<KB, VB, 2>(a, st);
 }
 
 template <int KB>
-static hipError_t launch_decode_k(const DecodeArgs& a, int qt, int vb, size_t lds, hipStream_t st) {
+static hipError_t launch_decode_k(const DecodeArgs& a, int qt, int vb, hipStream_t st) {
   switch (vb) {
-    case 2: return launch_decode_kv<KB, 2>(a, qt, lds, st);
-    case 3: return launch_decode_kv<KB, 3>(a, qt, lds, st);
-    case 4: return launch_decode_kv<KB, 4>(a, qt, lds, st);
-    case 5: return launch_decode_kv<KB, 5>(a, qt, lds, st);
+    case 2: return launch_decode_kv<KB, 2>(a, qt, st);
+    case 3: return launch_decode_kv<KB, 3>(a, qt, st);
+    case 4: return launch_decode_kv<KB, 4>(a, qt, st);
+    case 5: return launch_decode_kv<KB, 5>(a, qt, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, size_t lds_bytes,
-                         hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   switch (k_bits) {
-    case 2: return launch_decode_k<2>(a, q_dtype, v_bits, lds_bytes, stream);
-    case 3: return launch_decode_k<3>(a, q_dtype, v_bits, lds_bytes, stream);
-    case 4: return launch_decode_k<4>(a, q_dtype, v_bits, lds_bytes, stream);
-    case 5: return launch_decode_k<5>(a, q_dtype, v_bits, lds_bytes, stream);
+    case 2: return launch_decode_k<2>(a, q_dtype, v_bits, stream);
+    case 3: return launch_decode_k<3>(a, q_dtype, v_bits, stream);
+    case 4: return launch_decode_k<4>(a, q_dtype, v_bits, stream);
+    case 5: return launch_decode_k<5>(a, q_dtype, v_bits, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -12,6 +12,7 @@
 #include "tq.h"
 #include "tq_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -221,10 +222,11 @@ int device_cu_count() {
 }
 
 // Decode work split.  A workgroup covers kv_per_wg KV heads of one sequence
-// and pages_per_split of its pages: the whole page when the KV heads times
-// their query groups (ceil(group / 8) each) fit 16 waves, else the largest
-// divisor of num_kv_heads that does.  streams = 16 / (kv_per_wg * q_groups)
-// waves share out the pages.  The split count aims at one workgroup per CU
+// and pages_per_split of its pages; its waves are kv_per_wg * q_groups
+// (ceil(group / 8) query groups per KV head) times streams, each wave taking
+// every streams-th page for one (KV head, query group).  Each wave keeps two
+// LDS page slots of its head's rows beside the lookup tables, which bounds
+// the waves per workgroup.  The split count aims at one workgroup per CU
 // (a workgroup fills a CU's LDS), keeps at least 8 splits for the longest
 // sequence (so ragged batches balance) and at most 64 (the merge holds one
 // split weight per lane).
@@ -240,20 +242,34 @@ struct SplitPlan {
 constexpr int kMaxWavesPerWg = 16;
 constexpr int kLdsBytes = tq::kDecodeLdsBytes;
 
-SplitPlan plan_split(int batch, int num_kv_heads, int group, int max_seq_len, int num_cus) {
+int row_window_page_bytes(int bits) {  // LDS bytes of one page of one head's rows
+  const int rb = (int)tq_row_bytes(kHeadDim, bits);
+  return tq::kBlockSize * 16 * ((rb + 12 + 15) / 16);
+}
+
+bool plan_split(int batch, int num_kv_heads, int group, int max_seq_len, int k_bits, int v_bits, int num_cus,
+                SplitPlan* out) {
   SplitPlan p;
   p.q_groups = (group + 7) / 8;
-  p.kv_per_wg = 1;
+  const int slot = row_window_page_bytes(k_bits) + row_window_page_bytes(v_bits);
+  // the split's block ids (4 bytes per page) share the LDS with the tables
+  const int max_pages_all = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
+  const int bt_cap = std::min((max_pages_all + 7) / 8, std::max(2048, (max_pages_all + 63) / 64));
+  const int bt_reserve = 4 * bt_cap + 16;
+  const int avail = kLdsBytes - tq::decode_table_bytes(k_bits, v_bits) - bt_reserve;
+  const int max_waves = avail / (2 * slot) < kMaxWavesPerWg ? avail / (2 * slot) : kMaxWavesPerWg;
+  p.kv_per_wg = 0;
   for (int h = 1; h <= num_kv_heads; ++h)
-    if (num_kv_heads % h == 0 && h * p.q_groups <= kMaxWavesPerWg) p.kv_per_wg = h;
+    if (num_kv_heads % h == 0 && h * p.q_groups <= max_waves) p.kv_per_wg = h;
+  if (p.kv_per_wg == 0) return false;
   p.head_groups = num_kv_heads / p.kv_per_wg;
-  p.streams = kMaxWavesPerWg / (p.kv_per_wg * p.q_groups);
-  if (p.streams < 1) p.streams = 1;
+  p.streams = max_waves / (p.kv_per_wg * p.q_groups);
   const int max_pages = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
   if (max_pages <= 0) {
     p.pages_per_split = 1;
     p.num_splits = 1;
-    return p;
+    *out = p;
+    return true;
   }
   const long long units = (long long)batch * p.head_groups;
   const long long target = num_cus;
@@ -262,71 +278,13 @@ SplitPlan plan_split(int batch, int num_kv_heads, int group, int max_seq_len, in
   long long pps = (max_pages + s0 - 1) / s0;
   const long long cap = (max_pages + 7) / 8;
   if (pps > cap) pps = cap;
+  if (pps > bt_cap) pps = bt_cap;
   const long long floor_pps = (max_pages + 63) / 64;
   if (pps < floor_pps) pps = floor_pps;
   if (pps < 1) pps = 1;
   p.pages_per_split = (int)pps;
   p.num_splits = (int)((max_pages + pps - 1) / pps);
-  return p;
-}
-
-// LDS geometry of the page ring for one (plan, bit widths): the staged
-// bytes of a page's rows, the 1 KB copies they take, and how many page
-// slots fit beside the lookup tables and the block ids.  The kernel issues
-// the copies of iteration i + 1's pages during iteration i, so the ring
-// needs at least 2 * streams slots; fewer streams are used when they do not
-// fit, and at most 3 * streams slots are used.
-struct RingPlan {
-  int streams;
-  int ring_pages;
-  int per_token;
-  int region[2], chunks[2], instr[2], tok_chunks[2], tstride[2];
-  int slot_bytes;
-  int bt_base;
-  size_t lds_bytes;
-};
-
-bool plan_ring(const SplitPlan& sp, int num_kv_heads, int k_row_bytes, int v_row_bytes, int k_bits, int v_bits,
-               RingPlan* out) {
-  RingPlan r;
-  r.per_token = sp.kv_per_wg < num_kv_heads;
-  const int rb[2] = {k_row_bytes, v_row_bytes};
-  for (int i = 0; i < 2; ++i) {
-    if (!r.per_token) {
-      r.chunks[i] = num_kv_heads * rb[i];  // a whole page, 16 * Hkv * row / 16
-      r.tok_chunks[i] = 0;
-      r.tstride[i] = num_kv_heads * rb[i];
-    } else {
-      // the slice of a token starts 4-byte aligned: copy the 16-byte chunks
-      // that cover it (at most 12 leading bytes more)
-      r.tok_chunks[i] = (sp.kv_per_wg * rb[i] + 12 + 15) / 16;
-      r.chunks[i] = tq::kBlockSize * r.tok_chunks[i];
-      r.tstride[i] = 16 * r.tok_chunks[i];
-    }
-    r.region[i] = 16 * r.chunks[i];
-    r.instr[i] = (r.chunks[i] + 63) / 64;
-  }
-  r.slot_bytes = r.region[0] + r.region[1];
-  const int tables = tq::decode_table_bytes(k_bits, v_bits);
-  const int bt_bytes = (4 * sp.pages_per_split + 15) & ~15;
-  const int avail = kLdsBytes - tables - bt_bytes;
-  r.streams = sp.streams;
-  for (;;) {
-    const int slots = avail > 0 ? avail / r.slot_bytes : 0;
-    const int want = 3 * r.streams;
-    if (slots >= 2 * r.streams) {
-      r.ring_pages = slots < want ? slots : want;
-      break;
-    }
-    if (r.streams == 1) return false;
-    r.streams /= 2;
-  }
-  // tables at 0, ring after them, block ids last
-  r.bt_base = tables + r.ring_pages * r.slot_bytes;
-  size_t lds = (size_t)r.bt_base + bt_bytes;
-  const size_t merge = (size_t)tq::decode_merge_lds_bytes();
-  r.lds_bytes = lds > merge ? lds : merge;
-  *out = r;
+  *out = p;
   return true;
 }
 
@@ -429,8 +387,17 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads, 
   (void)ctx;
   (void)block_size;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
-  SplitPlan p = plan_split(batch, num_kv_heads, num_q_heads / num_kv_heads, max_seq_len, device_cu_count());
-  size_t per = (size_t)batch * num_q_heads * p.num_splits;
+  // the split count depends on the bit widths through the LDS budget: size
+  // for the largest over every supported pair
+  int splits = 1;
+  for (int kb = 2; kb <= 5; ++kb)
+    for (int vb = 2; vb <= 5; ++vb) {
+      SplitPlan p;
+      if (plan_split(batch, num_kv_heads, num_q_heads / num_kv_heads, max_seq_len, kb, vb, device_cu_count(), &p) &&
+          p.num_splits > splits)
+        splits = p.num_splits;
+    }
+  size_t per = (size_t)batch * num_q_heads * splits;
   return per * (kHeadDim + 1) * sizeof(float) + 256;
 }
 
@@ -459,15 +426,14 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
       tq_decode_workspace_bytes(ctx, batch, num_q_heads, num_kv_heads, max_seq_len, block_size);
   if (!workspace || workspace_bytes < need) return TQ_ERR_WORKSPACE;
 
-  SplitPlan p = plan_split(batch, num_kv_heads, group, max_seq_len, device_cu_count());
+  SplitPlan p;
+  if (!plan_split(batch, num_kv_heads, group, max_seq_len, k_bits, v_bits, device_cu_count(), &p))
+    return TQ_ERR_UNSUPPORTED;
   const float sm_scale = scale > 0 ? scale : 1.0f / std::sqrt((float)kHeadDim);
   const float k_scale = ctx->tab_scale[k_bits];
   const float v_scale = ctx->tab_scale[v_bits];
-
   const int k_row_bytes = (int)tq_row_bytes(kHeadDim, k_bits);
   const int v_row_bytes = (int)tq_row_bytes(kHeadDim, v_bits);
-  RingPlan rp;
-  if (!plan_ring(p, num_kv_heads, k_row_bytes, v_row_bytes, k_bits, v_bits, &rp)) return TQ_ERR_UNSUPPORTED;
 
   tq::DecodeArgs d;
   std::memset(&d, 0, sizeof(d));
@@ -490,27 +456,10 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   d.max_blocks_per_seq = max_blocks_per_seq;
   d.kv_per_wg = p.kv_per_wg;
   d.head_groups = p.head_groups;
-  d.streams = rp.streams;
-  d.waves = p.kv_per_wg * p.q_groups * rp.streams;
+  d.streams = p.streams;
+  d.waves = p.kv_per_wg * p.q_groups * p.streams;
   d.pages_per_split = p.pages_per_split;
   d.num_splits = p.num_splits;
-  d.ring_pages = rp.ring_pages;
-  d.slot_bytes = rp.slot_bytes;
-  d.bt_base = rp.bt_base;
-  d.per_token = rp.per_token;
-  d.dmask = rp.per_token ? 15 : 0;
-  d.k_region = rp.region[0];
-  d.v_region = rp.region[1];
-  d.k_chunks = rp.chunks[0];
-  d.v_chunks = rp.chunks[1];
-  d.k_instr = rp.instr[0];
-  d.v_instr = rp.instr[1];
-  d.k_tok_chunks = rp.tok_chunks[0];
-  d.v_tok_chunks = rp.tok_chunks[1];
-  d.k_tstride = rp.tstride[0];
-  d.v_tstride = rp.tstride[1];
-  d.k_inv_tok_chunks = rp.tok_chunks[0] ? 1.0f / (float)rp.tok_chunks[0] : 0.0f;
-  d.v_inv_tok_chunks = rp.tok_chunks[1] ? 1.0f / (float)rp.tok_chunks[1] : 0.0f;
   d.q_scale = (float)((double)sm_scale * 1.4426950408889634 / (std::sqrt((double)kHeadDim) * k_scale));
   std::memcpy(d.sign_bits, ctx->sign_bits, sizeof(d.sign_bits));
   for (int j = 0; j < (1 << k_bits); ++j) d.k_cent[j] = ctx->cent[k_bits][j] * k_scale;
@@ -518,7 +467,7 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   // per-page byte offsets are 32-bit inside a page
   if (d.k_page_bytes > (1 << 30) || d.v_page_bytes > (1 << 30)) return TQ_ERR_UNSUPPORTED;
 
-  tq_status st = hip_status(tq::launch_decode(d, (int)q_dtype, k_bits, v_bits, rp.lds_bytes, (hipStream_t)stream));
+  tq_status st = hip_status(tq::launch_decode(d, (int)q_dtype, k_bits, v_bits, (hipStream_t)stream));
   if (st != TQ_OK) return st;
 
   tq::MergeArgs m;

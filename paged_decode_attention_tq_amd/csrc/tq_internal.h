@@ -29,11 +29,10 @@ struct WriteArgs {
 };
 
 // Arguments of the decode split kernel.  One workgroup handles one
-// (sequence, group of kv_per_wg KV heads, split of pages_per_split pages).
-// It copies the pages' rows of its KV heads into a ring of LDS page slots
-// and runs waves = kv_per_wg * q_groups * streams waves: each wave owns one
-// KV head, one group of up to 8 of its query heads, and every streams-th
-// page of the split.
+// (sequence, group of kv_per_wg KV heads, split of pages_per_split pages)
+// with waves = kv_per_wg * q_groups * streams waves: each wave owns one KV
+// head, one group of up to 8 of its query heads, and every streams-th page
+// of the split, whose rows of its head it copies into LDS itself.
 struct DecodeArgs {
   const void* q;                 // [B, Hq, 128]
   const uint8_t* k_pages;
@@ -54,23 +53,10 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int32_t kv_per_wg;             // KV heads of one workgroup
   int32_t head_groups;           // num_kv_heads / kv_per_wg
-  int32_t streams;               // pages computed per iteration
+  int32_t streams;               // waves sharing out the pages of one (head, query group)
   int32_t waves;                 // kv_per_wg * q_groups * streams (<= 16)
   int32_t pages_per_split;       // pages per workgroup
   int32_t num_splits;            // S
-  int32_t ring_pages;            // LDS page slots (> streams)
-  int32_t slot_bytes;            // k_region + v_region
-  int32_t bt_base;               // LDS byte offset of the split's block ids
-  int32_t per_token;             // 0: whole page copied (kv_per_wg == num_kv_heads)
-                                 // 1: per-token slices of the workgroup's heads
-  int32_t dmask;                 // 15 in per-token mode, else 0
-  // per component (K, V):
-  int32_t k_region, v_region;    // LDS bytes of one page's staged rows
-  int32_t k_chunks, v_chunks;    // 16-byte chunks copied per page
-  int32_t k_instr, v_instr;      // ceil(chunks / 64): 1 KB copies per page
-  int32_t k_tok_chunks, v_tok_chunks;  // per-token mode: chunks per token
-  int32_t k_tstride, v_tstride;  // LDS bytes between consecutive tokens
-  float k_inv_tok_chunks, v_inv_tok_chunks;
   float q_scale;                 // softmax scale * log2(e) / (sqrt(128) * k_scale)
   uint32_t sign_bits[kHeadDim / 32];
   float k_cent[32];              // fp32 centroids of K times k_scale
@@ -92,8 +78,7 @@ struct MergeArgs {
 };
 
 hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, size_t lds_bytes,
-                         hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, hipStream_t stream);
 int decode_table_bytes(int k_bits, int v_bits);  // LDS bytes of the decode lookup tables
 int decode_merge_lds_bytes();                     // LDS bytes of the stream merge
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
