@@ -35,50 +35,80 @@ def log(msg):
 
 
 def cpu_baseline(w, kraw, vraw, q, seconds=15.0):
-    """Time the oracle (as it stands) on one sequence, a subset of KV heads."""
+    """Time the oracle, as it stands, on a bounded sample of the workload.
+
+    The sample is the first ``Ls`` tokens of sequence 0 (all KV heads): the
+    oracle writer builds its pages, then ``oracle.paged_decode_heads`` decodes
+    whole query groups until about ``seconds`` have been spent.  The decode
+    time of one group is scaled to a full step (every group of every
+    sequence, at the full context length).
+    """
     import oracle
 
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl is optional
+        blas_threads = None
     codec = oracle.OracleCodec(w.head_dim, w.rht_seed)
-    ck, cv = codec.centroids32(w.k_bits), codec.centroids32(w.v_bits)
-    b = 0
-    L = int(w.seq_lens[b])
+    L = int(w.seq_lens[0])
+    Ls = min(L, 32768)
     G = w.num_q_heads // w.num_kv_heads
-    lo = int(w.cu_seqlens[b])
-    t_total, groups = 0.0, 0
+    lo = int(w.cu_seqlens[0])
+    npg = (Ls + w.block_size - 1) // w.block_size
+    bt = np.arange(npg, dtype=np.int32)[None]
+    slots = np.arange(Ls, dtype=np.int64)
+    kp = np.zeros((npg, w.block_size, w.num_kv_heads, w.row_bytes(w.k_bits)), dtype=np.uint8)
+    vp = np.zeros((npg, w.block_size, w.num_kv_heads, w.row_bytes(w.v_bits)), dtype=np.uint8)
     t0 = time.perf_counter()
+    kp, _ = codec.write_kv(kraw[lo:lo + Ls], kp, slots, w.k_bits)
+    vp, _ = codec.write_kv(vraw[lo:lo + Ls], vp, slots, w.v_bits)
+    t_write = time.perf_counter() - t0
+    ck, cv = codec.centroids32(w.k_bits), codec.centroids32(w.v_bits)
+    t_dec, groups = 0.0, 0
     for g in range(w.num_kv_heads):
-        # encode this KV head's rows of sequence b (the oracle writer), then decode its query heads
+        heads = [(0, h) for h in range(g * G, (g + 1) * G)]
         ts = time.perf_counter()
-        krows, _ = codec.encode_bytes(kraw[lo:lo + L, g], w.k_bits)
-        vrows, _ = codec.encode_bytes(vraw[lo:lo + L, g], w.v_bits)
-        t_enc = time.perf_counter() - ts
-        ts = time.perf_counter()
-        K = codec.dequantize(krows, w.k_bits)
-        V = codec.dequantize(vrows, w.v_bits)
-        for h in range(g * G, (g + 1) * G):
-            s = (K @ q[b, h].astype(np.float64)) / np.sqrt(w.head_dim)
-            p = np.exp(s - s.max())
-            _ = (p / p.sum()) @ V
-        t_total += time.perf_counter() - ts
+        oracle.paged_decode_heads(q[:1], kp, vp, bt, np.array([Ls]), w.k_bits, w.v_bits, codec.signs, ck, cv, heads)
+        t_dec += time.perf_counter() - ts
         groups += 1
-        del t_enc
-        if time.perf_counter() - t0 > seconds:
+        if t_dec > seconds:
             break
-    t_seq = t_total / groups * w.num_kv_heads  # decode of one whole sequence (all heads)
-    bytes_seq = L * w.num_kv_heads * (w.row_bytes(w.k_bits) + w.row_bytes(w.v_bits))
+    t_group = t_dec / groups
+    t_step = t_group * w.num_kv_heads * w.batch * (L / Ls)  # every group of every sequence, full context
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
     return {
-        "value": 1.0 / t_seq,
+        "value": w.batch / t_step,
         "unit": "decode tokens/s",
-        "packed_kv_gbps": bytes_seq / t_seq / 1e9,
-        "cores": cores,
+        "packed_kv_gbps": w.packed_kv_bytes() / t_step / 1e9,
+        "cores": blas_threads if blas_threads else cores,
+        "host_cores": cores,
         "kind": "oracle",
-        "sample": f"sequence 0 ({L} tokens), {groups} of {w.num_kv_heads} KV heads x {G} query heads, "
-                  f"float64 dequantise-then-softmax, scaled to all heads",
+        "sample": f"sequence 0, first {Ls} of {L} tokens, {groups} of {w.num_kv_heads} KV-head groups x {G} query "
+                  f"heads decoded by oracle.paged_decode_heads (float64) in {t_dec:.1f} s, scaled to "
+                  f"{w.batch} sequences x {L} tokens x {w.num_kv_heads} groups; oracle write of the sample "
+                  f"({Ls} tokens x {w.num_kv_heads} heads, K and V) took {t_write:.1f} s",
     }
+
+
+def traffic_bytes():
+    """HBM bytes per decode call from the committed counter profile, if it was
+    taken on the current decode source (else None)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    src = os.path.join(ROOT, "paged_decode_attention_tq_amd", "csrc", "tq_decode.hip")
+    try:
+        prof = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if prof.get("tq_decode_hip_sha256") != digest:
+        return None
+    return prof.get("bytes_per_call")
 
 
 def main():
@@ -89,6 +119,7 @@ def main():
     ap.add_argument("--config", default="long_context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-flush", action="store_true", help="skip the 1 GiB cache flush before each timed decode")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -133,17 +164,24 @@ def main():
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     del kraw_d, vraw_d
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # writing 1 GiB before each timed decode evicts the pages from L2 and the 256 MB MALL
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     def step(i=None):
+        # timed: the row writer for the new token of every sequence, then the decode
+        if flush is not None:
+            flush.zero_()
+        if i is not None:
+            ev[i][0].record()
         api.write_kv(ctx, k_new, kp, new_slots, w.k_bits, err_count=err, check_slots=False)
         api.write_kv(ctx, v_new, vp, new_slots, w.v_bits, err_count=err, check_slots=False)
         if i is not None:
-            ev[i][0].record()
+            ev[i][1].record()
         api.paged_decode(ctx, q_d, kp, vp, bt, lens, w.k_bits, w.v_bits, max_seq_len=w.max_seq_len,
                          out=out, workspace=ws)
         if i is not None:
-            ev[i][1].record()
+            ev[i][2].record()
 
     for _ in range(args.warmup):
         step()
@@ -154,10 +192,13 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     assert int(err.item()) == 0
-    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in ev])
     log(f"[bench] decode ms per call: mean {dec_ms.mean():.4f} median {np.median(dec_ms):.4f} min {dec_ms.min():.4f}")
 
-    ms_step = elapsed * 1e3 / args.steps
+    ms_step = float(step_ms.mean())
+    log(f"[bench] step (write + decode) ms: mean {ms_step:.4f}; wall per step incl. cache flush "
+        f"{elapsed * 1e3 / args.steps:.4f}")
     packed = w.packed_kv_bytes()
     dec_s = float(dec_ms.mean()) / 1e3
     achieved = packed / dec_s / 1e9
@@ -194,7 +235,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": traffic_bytes(),
         },
         "cpu_baseline": None,
     }

@@ -36,6 +36,7 @@
 #include "tq_device.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace tq {
 
@@ -99,11 +100,10 @@ __device__ __forceinline__ uint32_t lds_u32(const uint8_t* base, uint32_t off) {
   return *reinterpret_cast<const uint32_t*>(base + off);
 }
 
-template <int QT>
-__device__ __forceinline__ float load_q(const void* q, int64_t i) {
-  if constexpr (QT == 0) return static_cast<const float*>(q)[i];
-  else if constexpr (QT == 1) return (float)static_cast<const _Float16*>(q)[i];
-  else return bf16_to_f32(static_cast<const uint16_t*>(q)[i]);
+__device__ __forceinline__ float load_q(const void* q, int64_t i, int qt) {
+  if (qt == 0) return static_cast<const float*>(q)[i];
+  if (qt == 1) return (float)static_cast<const _Float16*>(q)[i];
+  return bf16_to_f32(static_cast<const uint16_t*>(q)[i]);
 }
 
 template <int R>
@@ -123,83 +123,31 @@ __device__ __forceinline__ float row_ror8(float v) {  // lane n <-> n ^ 8 inside
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
 }
 
-// ---------------------------------------------------------------------------
-// Page copies into LDS.  One buffer_load_dwordx4 with the lds modifier moves
-// 64 16-byte chunks (1 KB) from global memory straight into LDS at
-// M0 + 16 * lane, without passing through registers.  It is issued from
-// inline assembly so that the compiler does not treat the later LDS reads
-// of other slots as depending on it; the kernel waits for the copies itself
-// (s_waitcnt vmcnt) before the barrier that publishes a page.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+#ifndef TQ_WG_WAVES
+#define TQ_WG_WAVES 16
+#endif
+#ifndef TQ_AHEAD
+#define TQ_AHEAD 1
+#endif
+constexpr int kMaxWaves = TQ_WG_WAVES;   // waves per workgroup (one workgroup per CU)
+constexpr int kWgThreads = 64 * kMaxWaves;
+constexpr int kAhead = TQ_AHEAD;         // stages of loads in flight
 
-__device__ __forceinline__ i32x4 buffer_rsrc(const uint8_t* base, uint32_t bytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r.x = (int)(uint32_t)p;
-  r.y = (int)((uint32_t)(p >> 32) & 0xFFFFu);
-  r.z = (int)bytes;
-  r.w = 0x00020000;
-  return r;
-}
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy_chunk_to_lds(i32x4 rsrc, uint32_t lds_addr, uint32_t src_off) {
-  // both are uniform by construction; readfirstlane makes that visible
-  rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
-  rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
-  rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
-  rsrc.w = __builtin_amdgcn_readfirstlane(rsrc.w);
-  lds_addr = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(lds_addr), "v"(src_off), "s"(rsrc)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// s_waitcnt vmcnt(n) (n clamped to 15, which only waits longer).  Written
-// as assembly with a memory clobber so that no LDS read of the page being
-// waited for is scheduled above it.
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-#define TQ_VM(k) \
-  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
-    TQ_VM(0) TQ_VM(1) TQ_VM(2) TQ_VM(3) TQ_VM(4) TQ_VM(5) TQ_VM(6) TQ_VM(7)
-    TQ_VM(8) TQ_VM(9) TQ_VM(10) TQ_VM(11) TQ_VM(12) TQ_VM(13) TQ_VM(14)
-#undef TQ_VM
-    default: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
-  }
-}
-
-// A row of a b-bit component in LDS: the 16-byte chunks of the window that
-// covers it (at most 12 bytes before its start), C of them per token.
-template <int B>
-struct RowWindow {
-  static constexpr int kRowBytes = (kHeadDim * B + 7) / 8 + 4;
-  static constexpr int kChunks = (kRowBytes + 12 + 15) / 16;
-  static constexpr int kPageBytes = kBlockSize * 16 * kChunks;           // one page of one head
-  static constexpr int kLoads = (kBlockSize * kChunks + 63) / 64;        // 1 KB loads per page
-  static constexpr int kLastLanes = kBlockSize * kChunks - 64 * (kLoads - 1);
-};
-
-constexpr int kMaxWaves = 16;
-
-template <int KB, int VB, int QT>
-__global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
+// CONTIG: the workgroup holds every KV head, so a page is staged as the
+// contiguous bytes it is; else per-token chunk windows over the slice of the
+// workgroup's heads.  MAXLD: 1 KB loads per wave per stage.
+template <int KB, int VB, bool CONTIG, int MAXLD>
+__global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) {
   // all of the CU's LDS, statically: addresses are then known constants
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDecodeLdsBytes];
   using KT = PairTable<KB>;
   using VT = PairTable<VB>;
-  using KS = RowWindow<KB>;
-  using VS = RowWindow<VB>;
   constexpr bool kShareV = (KB == VB);
-  // LDS: lookup tables at 0 (so their addresses need no base), then one
-  // two-slot ring per wave
+  // LDS: lookup tables at 0 (so their addresses need no base), then two
+  // stage slots, then the split's block ids
   constexpr int kVTab = 0;
   constexpr int kKTab = kShareV ? 0 : VT::kBytes;
-  constexpr int kRing = kKTab + KT::kBytes;
-  constexpr int kSlot = KS::kPageBytes + VS::kPageBytes;  // one page of one KV head
+  constexpr int kStages = kKTab + KT::kBytes;
 
   const int S = a.num_splits;
   const int unit = __builtin_amdgcn_workgroup_id_x();
@@ -214,7 +162,7 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   const int span = min(a.pages_per_split, npages - p0);
 
   // the wave index is uniform; say so, so that everything derived from it
-  // (head, page stream, ring) lives in scalar registers
+  // (head, page stream, load assignment) lives in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int W = a.waves;
@@ -223,7 +171,8 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   const int hs = wave - st * hpw;
   const int kvl = hs / a.q_groups;
   const int qgi = hs - kvl * a.q_groups;
-  const int g = hg * a.kv_per_wg + kvl;        // KV head
+  const int g0 = hg * a.kv_per_wg;
+  const int g = g0 + kvl;                      // KV head
   const int qh0 = g * a.group + qgi * 8;
   const int gsz = min(8, a.group - qgi * 8);   // query heads of this wave
   const int n = lane & 15;
@@ -231,56 +180,95 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   const int hq = n & 7;                        // query head (within the wave's group) of column n
   const int par = n >> 3;                      // column half: q_lo / odd value dims
   const int strm = a.streams;
-  // this wave's pages: st, st + strm, ... of the split
-  const int n_my = span > st ? (span - st + strm - 1) / strm : 0;
+  const int32_t* bt_lds = reinterpret_cast<const int32_t*>(lds + a.bt_base);
 
-  const uint32_t lds0 = (uint32_t)(size_t)((__attribute__((address_space(3))) uint8_t*)lds);
-
-  // ---- page copies ------------------------------------------------------------
-  // Each wave copies the rows of its own KV head, and only those, into its
-  // own two LDS slots: K then V, token t at t * 16C + delta_t, where the
-  // 16-byte window of C chunks covering the row starts delta_t bytes before
-  // it.  No other wave reads them, so the wave only waits for its own loads.
-  const uint32_t ring = (uint32_t)(kRing + wave * 2 * kSlot);
+  // ---- staging geometry --------------------------------------------------------
+  // A stage is strm consecutive pages (one per stream) of the workgroup's
+  // heads; two stage slots alternate.  A page slot holds the K part, then the
+  // V part.  CONTIG: each part is the page's bytes as they are (token t of
+  // head g at t * Hkv * RB + g * RB).  Else the slice of the workgroup's heads
+  // for token t (kv_per_wg * RB bytes) is staged as the C 16-byte chunks of a
+  // window that covers it and starts delta_t (at most 31) bytes before it:
+  // token t at t * 16C + delta_t.
   const int k_rows = (int)a.k_page_bytes, v_rows = (int)a.v_page_bytes;
-  // window start and row start of token t in a page
+  const int kC = a.k_tok_chunks, vC = a.v_tok_chunks;
   auto window = [&](int t, int RB, int C, int page_bytes, int& delta) {
-    const int row = (t * a.num_kv_heads + g) * RB;
+    const int row = (t * a.num_kv_heads + g0) * RB;
     int w = row & ~15;
     if (w + 16 * C > page_bytes) w = page_bytes - 16 * C;
     delta = row - w;
     return w;
   };
-  // per-lane source offsets of the (at most two) 1 KB loads per component
-  uint32_t k_src[2], v_src[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    int d;
-    const int jk = 64 * q + lane, tk = jk / KS::kChunks;
-    k_src[q] = (uint32_t)(window(min(tk, kBlockSize - 1), a.k_row_bytes, KS::kChunks, k_rows, d) + 16 * (jk - tk * KS::kChunks));
-    if constexpr (KB == VB) {
-      v_src[q] = k_src[q];  // same row size, same page size: same windows
+  // Load x of a stage (0 <= x < strm * (nk + nv)) is 64 chunks of page
+  // x / (nk + nv): K chunks 64 r .. 64 r + 63 for r = x % (nk + nv) < nk,
+  // else V.  Wave w issues loads w, w + W, ... (at most MAXLD).
+  const int nk = a.k_loads, nkv = a.k_loads + a.v_loads;
+  const int n_ld = strm * nkv > wave ? (strm * nkv - wave + W - 1) / W : 0;
+  const uint32_t lane16 = 16u * (uint32_t)lane;
+  auto load_src = [&](int d) -> uint32_t {  // lane's source offset inside the page
+    const int x = wave + d * W;
+    const int r = x % nkv;
+    const bool isv = r >= nk;
+    const int ri = isv ? r - nk : r;
+    if constexpr (CONTIG) {
+      return (uint32_t)(ri * 1024) + lane16;
     } else {
-      const int jv = 64 * q + lane, tv = jv / VS::kChunks;
-      v_src[q] = (uint32_t)(window(min(tv, kBlockSize - 1), a.v_row_bytes, VS::kChunks, v_rows, d) + 16 * (jv - tv * VS::kChunks));
+      const int C = isv ? vC : kC;
+      const int ch = min(ri * 64 + lane, kBlockSize * C - 1);
+      const int t = ch / C;
+      int dl;
+      return (uint32_t)(window(t, isv ? a.v_row_bytes : a.k_row_bytes, C, isv ? v_rows : k_rows, dl) + 16 * (ch - t * C));
     }
-  }
-  // the split's block ids are staged in LDS after the rings
-  const int32_t* bt_lds = reinterpret_cast<const int32_t*>(lds + kRing + W * 2 * kSlot);
-  auto issue_page = [&](int i) {  // this wave's page i into slot i & 1
-    const int blk = __builtin_amdgcn_readfirstlane(bt_lds[st + strm * i]);
-    const uint32_t dst = lds0 + ring + (uint32_t)((i & 1) * kSlot);
-    const i32x4 kr = buffer_rsrc(a.k_pages + (int64_t)blk * a.k_page_bytes, (uint32_t)k_rows);
-#pragma unroll
-    for (int q = 0; q < KS::kLoads; ++q)
-      if (q + 1 < KS::kLoads || lane < KS::kLastLanes) copy_chunk_to_lds(kr, dst + 1024u * q, k_src[q]);
-    const i32x4 vr = buffer_rsrc(a.v_pages + (int64_t)blk * a.v_page_bytes, (uint32_t)v_rows);
-#pragma unroll
-    for (int q = 0; q < VS::kLoads; ++q)
-      if (q + 1 < VS::kLoads || lane < VS::kLastLanes)
-        copy_chunk_to_lds(vr, dst + (uint32_t)KS::kPageBytes + 1024u * q, v_src[q]);
   };
-  constexpr int kLoadsPerPage = KS::kLoads + VS::kLoads;
+  auto load_lanes = [&](int d) {  // lanes below this carry a chunk
+    const int x = wave + d * W;
+    const int r = x % nkv;
+    const bool isv = r >= nk;
+    const int ri = isv ? r - nk : r;
+    return (isv ? a.v_chunks : a.k_chunks) - ri * 64;
+  };
+  uint32_t ld_src[MAXLD];
+#pragma unroll
+  for (int d = 0; d < MAXLD; ++d) ld_src[d] = CONTIG ? 0u : load_src(d);
+  // kAhead register sets: stage si lives in set si % kAhead
+  u32x4 stage_regs[kAhead][MAXLD];
+  auto issue_loads = [&](int si, auto set_tag) {  // global loads of stage si into registers
+    constexpr int SET = decltype(set_tag)::value;
+#pragma unroll
+    for (int d = 0; d < MAXLD; ++d) {
+      // lanes and loads left out are left out of write_stage as well
+      if (d < n_ld) {
+        const int x = wave + d * W;
+        const int P = si * strm + x / nkv;
+        if (P < span) {
+          const bool isv = (x % nkv) >= nk;
+          const int blk = __builtin_amdgcn_readfirstlane(bt_lds[P]);
+          const uint8_t* base = isv ? a.v_pages + (int64_t)blk * a.v_page_bytes : a.k_pages + (int64_t)blk * a.k_page_bytes;
+          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
+                                                                              isv ? v_rows : k_rows, 0x00020000);
+          const uint32_t src = CONTIG ? load_src(d) : ld_src[d];
+          if (lane < load_lanes(d))
+            stage_regs[SET][d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, src, 0, 0));
+        }
+      }
+    }
+  };
+  auto write_stage = [&](int si, int slot, auto set_tag) {  // the registers of stage si into LDS slot
+    constexpr int SET = decltype(set_tag)::value;
+#pragma unroll
+    for (int d = 0; d < MAXLD; ++d) {
+      if (d < n_ld) {
+        const int x = wave + d * W;
+        const int j = x / nkv, r = x % nkv;
+        const bool isv = r >= nk;
+        const int ri = isv ? r - nk : r;
+        if (si * strm + j < span && lane < load_lanes(d)) {
+          const int off = kStages + slot * a.stage_bytes + j * a.page_slot_bytes + (isv ? a.k_region : 0) + ri * 1024;
+          *reinterpret_cast<u32x4*>(lds + off + 16 * lane) = stage_regs[SET][d];
+        }
+      }
+    }
+  };
 
   // ---- rotated, scaled query as the B operand of the score MFMAs ----------
   // Lane (n, c) covers dims 32c..32c+31 (16 pairs); column n < 8 holds the
@@ -293,7 +281,7 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
     const int64_t qoff = ((int64_t)b * a.num_q_heads + qh0 + (has ? hq : 0)) * kHeadDim + 32 * c;
     float x[32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) x[j] = load_q<QT>(a.q, qoff + j);
+    for (int j = 0; j < 32; ++j) x[j] = load_q(a.q, qoff + j, a.q_dtype);
 #pragma unroll
     for (int j = 0; j < 32; ++j) x[j] = has ? x[j] : 0.0f;
     const uint32_t sw = a.sign_bits[c];
@@ -348,32 +336,46 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
   if constexpr (!kShareV) fill_pair_table<VB>(lds + kVTab, a.v_cent, tid, 64 * W);
   {
     const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0;
-    int32_t* dst = reinterpret_cast<int32_t*>(lds + kRing + W * 2 * kSlot);
+    int32_t* dst = reinterpret_cast<int32_t*>(lds + a.bt_base);
     for (int i = tid; i < span; i += 64 * W) dst[i] = bt[i];
   }
   __syncthreads();
 
-  // ---- per-lane LDS offsets inside a slot ---------------------------------------
+  // ---- per-lane LDS offsets inside a page slot ------------------------------------
   auto tok_k = [&](int t) {
-    int d;
-    (void)window(t, a.k_row_bytes, KS::kChunks, k_rows, d);
-    return (int)ring + t * 16 * KS::kChunks + d;
+    if constexpr (CONTIG) {
+      return t * a.num_kv_heads * a.k_row_bytes + g * a.k_row_bytes;
+    } else {
+      int d;
+      (void)window(t, a.k_row_bytes, kC, k_rows, d);
+      return t * 16 * kC + d + kvl * a.k_row_bytes;
+    }
   };
   auto tok_v = [&](int t) {
-    int d;
-    (void)window(t, a.v_row_bytes, VS::kChunks, v_rows, d);
-    return (int)ring + KS::kPageBytes + t * 16 * VS::kChunks + d;
+    if constexpr (CONTIG) {
+      return a.k_region + t * a.num_kv_heads * a.v_row_bytes + g * a.v_row_bytes;
+    } else {
+      int d;
+      (void)window(t, a.v_row_bytes, vC, v_rows, d);
+      return a.k_region + t * 16 * vC + d + kvl * a.v_row_bytes;
+    }
   };
   const int v_byte = n * VB;
   const int v_dat = (VB == 3 || VB == 5) ? (v_byte & ~3) : (v_byte & ~1);
-  const uint32_t k_idx_off = (uint32_t)(tok_k(n) + 4 * KB * c);
+  const uint32_t k_idx_off = (uint32_t)(kStages + tok_k(n) + 4 * KB * c);
   // each lane reads the norms of token 4c + (n & 3); quad broadcasts hand
   // every lane those of tokens 4c .. 4c + 3
-  const uint32_t k_norm_off = (uint32_t)(tok_k(4 * c + (n & 3)) + a.k_row_bytes - 4);
-  const uint32_t v_norm_off = (uint32_t)(tok_v(4 * c + (n & 3)) + a.v_row_bytes - 4);
-  uint32_t v_dat_off[4];
+  const uint32_t k_norm_off = (uint32_t)(kStages + tok_k(4 * c + (n & 3)) + a.k_row_bytes - 4);
+  const uint32_t v_norm_off = (uint32_t)(kStages + tok_v(4 * c + (n & 3)) + a.v_row_bytes - 4);
+  // value bytes of token 4c + r: CONTIG: base + r * token stride
+  const int v_tstride = a.num_kv_heads * a.v_row_bytes;
+  uint32_t v_dat_off[CONTIG ? 1 : 4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) v_dat_off[r] = (uint32_t)(tok_v(4 * c + r) + v_dat);
+  for (int r = 0; r < (CONTIG ? 1 : 4); ++r) v_dat_off[r] = (uint32_t)(kStages + tok_v(4 * c + r) + v_dat);
+  auto v_dat_at = [&](int r) -> uint32_t {
+    if constexpr (CONTIG) return v_dat_off[0] + (uint32_t)(r * v_tstride);
+    else return v_dat_off[r];
+  };
   const uint32_t v_shift = 8u * (uint32_t)(v_byte & 3);
   const uint32_t k_lane = (uint32_t)(lane & (KT::kRep - 1)) * 8u;
   // the hi dword of this lane's replica
@@ -391,31 +393,12 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
 
   auto compute_page = [&](uint32_t pg, int tok0, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
-    // pg: byte offset of the page slot from the ring start
+    // pg: byte offset of the page slot inside the stage area
+    // -- keys: indices, norms, (hi, lo) fp16 pairs of 16 dim pairs, scores.
     uint32_t kw[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) kw[i] = lds_u32(lds, pg + k_idx_off + 4 * i);
     const float nk_mine = __uint_as_float(lds_u32(lds, pg + k_norm_off));
-    const float nv_mine = __uint_as_float(lds_u32(lds, pg + v_norm_off));
-    float nk[4], nv[4];
-    nk[0] = quad_bcast<0>(nk_mine);
-    nk[1] = quad_bcast<1>(nk_mine);
-    nk[2] = quad_bcast<2>(nk_mine);
-    nk[3] = quad_bcast<3>(nk_mine);
-    nv[0] = quad_bcast<0>(nv_mine);
-    nv[1] = quad_bcast<1>(nv_mine);
-    nv[2] = quad_bcast<2>(nv_mine);
-    nv[3] = quad_bcast<3>(nv_mine);
-    uint32_t vw[4], vw2[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (VB == 2) {
-        vw[r] = *reinterpret_cast<const uint16_t*>(lds + pg + v_dat_off[r]);
-      } else {
-        vw[r] = lds_u32(lds, pg + v_dat_off[r]);
-        if constexpr (VB == 3 || VB == 5) vw2[r] = lds_u32(lds, pg + v_dat_off[r] + 4);
-      }
-    }
     uint32_t kh[16], kl[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -423,8 +406,31 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
       kh[k] = e[0];
       kl[k] = e[1];
     }
-    // -- value lookups: dword (V[t][2p], V[t][2p+1]) for pair p = 4n + blk of
-    // token 4c + j is exactly A[row n][k = 2j, 2j+1] of value block blk
+    // A = [K_hi(p), K_lo(p), K_hi(p'), K_lo(p')], B = [q(p), q(p), q(p'), q(p')]
+    floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const half8 A = __builtin_bit_cast(half8, u32x4{kh[2 * m], kl[2 * m], kh[2 * m + 1], kl[2 * m + 1]});
+      const half8 Bq = __builtin_bit_cast(half8, u32x4{qd[2 * m], qd[2 * m], qd[2 * m + 1], qd[2 * m + 1]});
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq, sc, 0, 0, 0);
+    }
+    // keep the value-side reads below the key side (register pressure)
+    __builtin_amdgcn_sched_barrier(0);
+    // -- values: norms, indices, and the lookups: dword (V[t][2p], V[t][2p+1])
+    // for pair p = 4n + blk of token 4c + j is exactly A[row n][k = 2j, 2j+1]
+    // of value block blk
+    const float nv_mine = __uint_as_float(lds_u32(lds, pg + v_norm_off));
+    uint32_t vw[4], vw2[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t vo = pg + v_dat_at(r);
+      if constexpr (VB == 2) {
+        vw[r] = *reinterpret_cast<const uint16_t*>(lds + vo);
+      } else {
+        vw[r] = lds_u32(lds, vo);
+        if constexpr (VB == 3 || VB == 5) vw2[r] = lds_u32(lds, vo + 4);
+      }
+    }
     uint32_t va[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -440,14 +446,15 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) va[blk][j] = lds_u32(v_tab, pair_addr<VB>(words, blk, v_lane));
     }
-    // -- scores: A = [K_hi(p), K_lo(p), K_hi(p'), K_lo(p')], B = [q(p), q(p), q(p'), q(p')]
-    floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const half8 A = __builtin_bit_cast(half8, u32x4{kh[2 * m], kl[2 * m], kh[2 * m + 1], kl[2 * m + 1]});
-      const half8 Bq = __builtin_bit_cast(half8, u32x4{qd[2 * m], qd[2 * m], qd[2 * m + 1], qd[2 * m + 1]});
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq, sc, 0, 0, 0);
-    }
+    float nk[4], nv[4];
+    nk[0] = quad_bcast<0>(nk_mine);
+    nk[1] = quad_bcast<1>(nk_mine);
+    nk[2] = quad_bcast<2>(nk_mine);
+    nk[3] = quad_bcast<3>(nk_mine);
+    nv[0] = quad_bcast<0>(nv_mine);
+    nv[1] = quad_bcast<1>(nv_mine);
+    nv[2] = quad_bcast<2>(nv_mine);
+    nv[3] = quad_bcast<3>(nv_mine);
     // -- softmax bookkeeping (log2 domain).  e = an upper bound of log2(n_v)
     // from the exponent bits (clamped so empty rows cannot blow up p).
     float full[4], xv[4];
@@ -493,27 +500,39 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
     }
   };
 
-  // ---- page loop ------------------------------------------------------------------
-  // Page i + 1 is copied while page i is computed.  The loads of a page are
-  // this wave's only memory operations in the loop, so "page i has landed"
-  // is "at most kLoadsPerPage loads outstanding".
-  auto iteration = [&](int i, auto full_tag) {
-    if (i + 1 < n_my) {
-      issue_page(i + 1);
-      wait_vmcnt(kLoadsPerPage);
-    } else {
-      wait_vmcnt(0);
-    }
-    const int P = st + strm * i;
-    compute_page((uint32_t)((i & 1) * kSlot), (p0 + P) * kBlockSize + 4 * c, full_tag);
+  // ---- stage loop ------------------------------------------------------------------
+  // Iteration i: barrier (stage i is in slot i & 1 for everyone, and every
+  // wave is done with slot (i + 1) & 1), store stage i + 1 from its
+  // registers into that slot, issue the loads of stage i + 1 + kAhead into
+  // the same registers, compute this wave's page of stage i.  kAhead stages
+  // of loads are in flight during the compute.
+  const int nit = (span + strm - 1) / strm;
+  using Set0 = std::integral_constant<int, 0>;
+  issue_loads(0, Set0{});
+  write_stage(0, 0, Set0{});
+  [&]<int... U>(std::integer_sequence<int, U...>) {
+    (issue_loads(1 + U, std::integral_constant<int, (1 + U) % kAhead>{}), ...);
+  }(std::make_integer_sequence<int, kAhead>{});
+  auto iteration = [&](int i, auto full_tag, auto set_tag) {  // set_tag: (i + 1) % kAhead
+    __syncthreads();
+    write_stage(i + 1, (i + 1) & 1, set_tag);
+    issue_loads(i + 1 + kAhead, set_tag);
+    const int P = strm * i + st;
+    if (P < span)
+      compute_page((uint32_t)((i & 1) * a.stage_bytes + st * a.page_slot_bytes), (p0 + P) * kBlockSize + 4 * c,
+                   full_tag);
   };
-  if (n_my > 0) {
-    issue_page(0);
-    // only the sequence's last page can be partial, and it is this wave's
-    // last page if this wave has it
-    for (int i = 0; i + 1 < n_my; ++i) iteration(i, std::true_type{});
-    iteration(n_my - 1, std::false_type{});
+  // only the sequence's last page can be partial, and it is in the last
+  // iteration: the others skip the masking
+  for (int i0 = 0; i0 + 1 < nit; i0 += kAhead) {
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      ((i0 + U + 1 < nit ? iteration(i0 + U, std::true_type{}, std::integral_constant<int, (U + 1) % kAhead>{})
+                         : void()), ...);
+    }(std::make_integer_sequence<int, kAhead>{});
   }
+  [&]<int... U>(std::integer_sequence<int, U...>) {
+    ((nit % kAhead == U ? iteration(nit - 1, std::false_type{}, std::integral_constant<int, U>{}) : void()), ...);
+  }(std::make_integer_sequence<int, kAhead>{});
 
   // ---- finish the split ---------------------------------------------------------
   float l_tot = l_part + __shfl_xor(l_part, 16);
@@ -547,8 +566,8 @@ __global__ __launch_bounds__(1024) void decode_split_kernel(DecodeArgs a) {
     return;
   }
 
-  // several streams per head: merge them through LDS (every copy has been
-  // waited for, so the rings and the tables are dead after the barrier)
+  // several streams per head: merge them through LDS (the stages and the
+  // tables are dead after the barrier)
   __syncthreads();
   float* m_buf = reinterpret_cast<float*>(lds);                   // [waves][8]
   float* l_buf = m_buf + kMaxWaves * 8;                           // [waves][8]
@@ -606,38 +625,40 @@ int decode_table_bytes(int k_bits, int v_bits) {
 
 int decode_merge_lds_bytes() { return kMaxWaves * 8 * (kHeadDim + 2) * 4; }
 
-template <int KB, int VB, int QT>
+template <int KB, int VB, bool CONTIG, int MAXLD>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const long long units = (long long)a.batch * a.head_groups * a.num_splits;
-  hipLaunchKernelGGL((decode_split_kernel<KB, VB, QT>), dim3((unsigned)units), dim3(64 * a.waves), 0, st, a);
+  hipLaunchKernelGGL((decode_split_kernel<KB, VB, CONTIG, MAXLD>), dim3((unsigned)units), dim3(64 * a.waves), 0, st, a);
   return hipGetLastError();
 }
 
 template <int KB, int VB>
-static hipError_t launch_decode_kv(const DecodeArgs& a, int qt, hipStream_t st) {
-  if (qt == 0) return launch_decode_t<KB, VB, 0>(a, st);
-  if (qt == 1) return launch_decode_t<KB, VB, 1>(a, st);
-  return launch_decode_t<KB, VB, 2>(a, st);
+static hipError_t launch_decode_kv(const DecodeArgs& a, hipStream_t st) {
+  const int per_wave = (a.streams * (a.k_loads + a.v_loads) + a.waves - 1) / a.waves;
+  const bool contig = a.kv_per_wg == a.num_kv_heads;
+  if (per_wave <= 3) return contig ? launch_decode_t<KB, VB, true, 3>(a, st) : launch_decode_t<KB, VB, false, 3>(a, st);
+  if (per_wave <= 4) return contig ? launch_decode_t<KB, VB, true, 4>(a, st) : launch_decode_t<KB, VB, false, 4>(a, st);
+  return hipErrorInvalidValue;
 }
 
 template <int KB>
-static hipError_t launch_decode_k(const DecodeArgs& a, int qt, int vb, hipStream_t st) {
+static hipError_t launch_decode_k(const DecodeArgs& a, int vb, hipStream_t st) {
   switch (vb) {
-    case 2: return launch_decode_kv<KB, 2>(a, qt, st);
-    case 3: return launch_decode_kv<KB, 3>(a, qt, st);
-    case 4: return launch_decode_kv<KB, 4>(a, qt, st);
-    case 5: return launch_decode_kv<KB, 5>(a, qt, st);
+    case 2: return launch_decode_kv<KB, 2>(a, st);
+    case 3: return launch_decode_kv<KB, 3>(a, st);
+    case 4: return launch_decode_kv<KB, 4>(a, st);
+    case 5: return launch_decode_kv<KB, 5>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   switch (k_bits) {
-    case 2: return launch_decode_k<2>(a, q_dtype, v_bits, stream);
-    case 3: return launch_decode_k<3>(a, q_dtype, v_bits, stream);
-    case 4: return launch_decode_k<4>(a, q_dtype, v_bits, stream);
-    case 5: return launch_decode_k<5>(a, q_dtype, v_bits, stream);
+    case 2: return launch_decode_k<2>(a, v_bits, stream);
+    case 3: return launch_decode_k<3>(a, v_bits, stream);
+    case 4: return launch_decode_k<4>(a, v_bits, stream);
+    case 5: return launch_decode_k<5>(a, v_bits, stream);
   }
   return hipErrorInvalidValue;
 }

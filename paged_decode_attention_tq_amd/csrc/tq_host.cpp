@@ -223,13 +223,13 @@ int device_cu_count() {
 
 // Decode work split.  A workgroup covers kv_per_wg KV heads of one sequence
 // and pages_per_split of its pages; its waves are kv_per_wg * q_groups
-// (ceil(group / 8) query groups per KV head) times streams, each wave taking
-// every streams-th page for one (KV head, query group).  Each wave keeps two
-// LDS page slots of its head's rows beside the lookup tables, which bounds
-// the waves per workgroup.  The split count aims at one workgroup per CU
-// (a workgroup fills a CU's LDS), keeps at least 8 splits for the longest
-// sequence (so ragged batches balance) and at most 64 (the merge holds one
-// split weight per lane).
+// (ceil(group / 8) query groups per KV head) times streams.  A stage is
+// `streams` pages of the workgroup's heads, staged as 16-byte chunk windows
+// over each token's slice; two stage slots, the lookup tables and the block
+// ids share the CU's LDS, which bounds kv_per_wg and streams.  The split
+// count aims at one workgroup per CU (a workgroup fills a CU's LDS), keeps at
+// least 8 splits for the longest sequence (so ragged batches balance) and at
+// most 64 (the merge holds one split weight per lane).
 struct SplitPlan {
   int q_groups;
   int kv_per_wg;
@@ -237,34 +237,59 @@ struct SplitPlan {
   int streams;
   int pages_per_split;
   int num_splits;
+  int tok_chunks[2];  // K, V
+  int chunks[2];
+  int loads[2];
+  int page_slot;
+  int bt_base;
 };
 
-constexpr int kMaxWavesPerWg = 16;
+#ifndef TQ_WG_WAVES
+#define TQ_WG_WAVES 16
+#endif
+constexpr int kMaxWavesPerWg = TQ_WG_WAVES;
+constexpr int kMaxLoadsPerWave = 4;
 constexpr int kLdsBytes = tq::kDecodeLdsBytes;
-
-int row_window_page_bytes(int bits) {  // LDS bytes of one page of one head's rows
-  const int rb = (int)tq_row_bytes(kHeadDim, bits);
-  return tq::kBlockSize * 16 * ((rb + 12 + 15) / 16);
-}
 
 bool plan_split(int batch, int num_kv_heads, int group, int max_seq_len, int k_bits, int v_bits, int num_cus,
                 SplitPlan* out) {
   SplitPlan p;
   p.q_groups = (group + 7) / 8;
-  const int slot = row_window_page_bytes(k_bits) + row_window_page_bytes(v_bits);
-  // the split's block ids (4 bytes per page) share the LDS with the tables
-  const int max_pages_all = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
-  const int bt_cap = std::min((max_pages_all + 7) / 8, std::max(2048, (max_pages_all + 63) / 64));
-  const int bt_reserve = 4 * bt_cap + 16;
-  const int avail = kLdsBytes - tq::decode_table_bytes(k_bits, v_bits) - bt_reserve;
-  const int max_waves = avail / (2 * slot) < kMaxWavesPerWg ? avail / (2 * slot) : kMaxWavesPerWg;
-  p.kv_per_wg = 0;
-  for (int h = 1; h <= num_kv_heads; ++h)
-    if (num_kv_heads % h == 0 && h * p.q_groups <= max_waves) p.kv_per_wg = h;
-  if (p.kv_per_wg == 0) return false;
-  p.head_groups = num_kv_heads / p.kv_per_wg;
-  p.streams = max_waves / (p.kv_per_wg * p.q_groups);
+  const int rb[2] = {(int)tq_row_bytes(kHeadDim, k_bits), (int)tq_row_bytes(kHeadDim, v_bits)};
+  const int tables = tq::decode_table_bytes(k_bits, v_bits);
   const int max_pages = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
+  const int bt_cap = std::max(1, std::min((max_pages + 7) / 8, std::max(2048, (max_pages + 63) / 64)));
+  const int bt_bytes = 4 * bt_cap;
+  bool found = false;
+  for (int kv = num_kv_heads; kv >= 1 && !found; --kv) {
+    if (num_kv_heads % kv || kv * p.q_groups > kMaxWavesPerWg) continue;
+    for (int i = 0; i < 2; ++i) {
+      if (kv == num_kv_heads) {  // whole pages, as they are
+        p.tok_chunks[i] = 0;
+        p.chunks[i] = num_kv_heads * rb[i];  // 16 * Hkv * RB / 16
+      } else {                   // window start at most 31 bytes before the slice
+        p.tok_chunks[i] = (kv * rb[i] + 16 + 15) / 16;
+        p.chunks[i] = tq::kBlockSize * p.tok_chunks[i];
+      }
+      p.loads[i] = (p.chunks[i] + 63) / 64;
+    }
+    p.page_slot = 16 * (p.chunks[0] + p.chunks[1]);
+    const int hpw = kv * p.q_groups;
+    for (int strm = kMaxWavesPerWg / hpw; strm >= 1; strm /= 2) {
+      const int waves = hpw * strm;
+      const int lds = tables + 2 * strm * p.page_slot + bt_bytes;
+      const int per_wave = (strm * (p.loads[0] + p.loads[1]) + waves - 1) / waves;
+      if (lds <= kLdsBytes && per_wave <= kMaxLoadsPerWave) {
+        p.kv_per_wg = kv;
+        p.streams = strm;
+        p.bt_base = tables + 2 * strm * p.page_slot;
+        found = true;
+        break;
+      }
+    }
+  }
+  if (!found) return false;
+  p.head_groups = num_kv_heads / p.kv_per_wg;
   if (max_pages <= 0) {
     p.pages_per_split = 1;
     p.num_splits = 1;
@@ -460,6 +485,17 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   d.waves = p.kv_per_wg * p.q_groups * p.streams;
   d.pages_per_split = p.pages_per_split;
   d.num_splits = p.num_splits;
+  d.q_dtype = (int)q_dtype;
+  d.k_tok_chunks = p.tok_chunks[0];
+  d.v_tok_chunks = p.tok_chunks[1];
+  d.k_chunks = p.chunks[0];
+  d.v_chunks = p.chunks[1];
+  d.k_loads = p.loads[0];
+  d.v_loads = p.loads[1];
+  d.k_region = 16 * p.chunks[0];
+  d.page_slot_bytes = p.page_slot;
+  d.stage_bytes = p.streams * p.page_slot;
+  d.bt_base = p.bt_base;
   d.q_scale = (float)((double)sm_scale * 1.4426950408889634 / (std::sqrt((double)kHeadDim) * k_scale));
   std::memcpy(d.sign_bits, ctx->sign_bits, sizeof(d.sign_bits));
   for (int j = 0; j < (1 << k_bits); ++j) d.k_cent[j] = ctx->cent[k_bits][j] * k_scale;
@@ -467,7 +503,7 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   // per-page byte offsets are 32-bit inside a page
   if (d.k_page_bytes > (1 << 30) || d.v_page_bytes > (1 << 30)) return TQ_ERR_UNSUPPORTED;
 
-  tq_status st = hip_status(tq::launch_decode(d, (int)q_dtype, k_bits, v_bits, (hipStream_t)stream));
+  tq_status st = hip_status(tq::launch_decode(d, k_bits, v_bits, (hipStream_t)stream));
   if (st != TQ_OK) return st;
 
   tq::MergeArgs m;

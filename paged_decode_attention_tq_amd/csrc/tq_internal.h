@@ -31,8 +31,9 @@ struct WriteArgs {
 // Arguments of the decode split kernel.  One workgroup handles one
 // (sequence, group of kv_per_wg KV heads, split of pages_per_split pages)
 // with waves = kv_per_wg * q_groups * streams waves: each wave owns one KV
-// head, one group of up to 8 of its query heads, and every streams-th page
-// of the split, whose rows of its head it copies into LDS itself.
+// head, one group of up to 8 of its query heads, and one page of every
+// stage (streams consecutive pages).  The workgroup loads each stage into
+// registers one iteration ahead and stores it into one of two LDS slots.
 struct DecodeArgs {
   const void* q;                 // [B, Hq, 128]
   const uint8_t* k_pages;
@@ -53,10 +54,20 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int32_t kv_per_wg;             // KV heads of one workgroup
   int32_t head_groups;           // num_kv_heads / kv_per_wg
-  int32_t streams;               // waves sharing out the pages of one (head, query group)
+  int32_t streams;               // pages per stage
   int32_t waves;                 // kv_per_wg * q_groups * streams (<= 16)
   int32_t pages_per_split;       // pages per workgroup
   int32_t num_splits;            // S
+  int32_t q_dtype;               // tq_dtype of q
+  // staging (per component): whole pages when kv_per_wg == num_kv_heads,
+  // else a token's slice of the workgroup's heads as C 16-byte chunks
+  int32_t k_tok_chunks, v_tok_chunks;  // C (slices only)
+  int32_t k_chunks, v_chunks;    // 16-byte chunks per page
+  int32_t k_loads, v_loads;      // 1 KB loads per page: ceil(chunks / 64)
+  int32_t k_region;              // LDS bytes of a page's K part: 16 k_chunks
+  int32_t page_slot_bytes;       // 16 (k_chunks + v_chunks)
+  int32_t stage_bytes;           // streams * page_slot_bytes
+  int32_t bt_base;               // LDS byte offset of the split's block ids
   float q_scale;                 // softmax scale * log2(e) / (sqrt(128) * k_scale)
   uint32_t sign_bits[kHeadDim / 32];
   float k_cent[32];              // fp32 centroids of K times k_scale
@@ -78,7 +89,7 @@ struct MergeArgs {
 };
 
 hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int k_bits, int v_bits, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, hipStream_t stream);
 int decode_table_bytes(int k_bits, int v_bits);  // LDS bytes of the decode lookup tables
 int decode_merge_lds_bytes();                     // LDS bytes of the stream merge
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
