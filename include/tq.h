@@ -142,8 +142,10 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  *   workspace    device, >= tq_decode_workspace_bytes(...) bytes, 16-byte
  *                aligned; contents are scratch.
  * Supported: head_dim 128, block_size 16, k_bits/v_bits 2..5,
- * num_q_heads / num_kv_heads in 1..16.  Asynchronous; block ids and lengths
- * are trusted (an out-of-range block id reads out of bounds). */
+ * num_q_heads / num_kv_heads in 1..64 (TQ_ERR_UNSUPPORTED otherwise, or when
+ * a sequence is so long that its block ids do not fit the on-chip plan).
+ * Asynchronous; block ids and lengths are trusted (an out-of-range block id
+ * reads out of bounds). */
 tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype,
                           int batch, int num_q_heads, int num_kv_heads,
                           const uint8_t* k_pages, int k_bits,
