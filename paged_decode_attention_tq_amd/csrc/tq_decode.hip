@@ -108,7 +108,15 @@ __device__ __forceinline__ float load_q(const void* q, int64_t i, int qt) {
 
 template <int R>
 __device__ __forceinline__ float quad_bcast(float v) {  // lane 4k + R of each quad to all four
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), R * 0x55, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), R * 0x55, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_bcast_r(float v, int r) {  // r: compile-time after unrolling
+  switch (r) {
+    case 0: return quad_bcast<0>(v);
+    case 1: return quad_bcast<1>(v);
+    case 2: return quad_bcast<2>(v);
+    default: return quad_bcast<3>(v);
+  }
 }
 
 // max over the four 16-lane rows (lanes n, n + 16, n + 32, n + 48)
@@ -126,12 +134,11 @@ __device__ __forceinline__ float row_ror8(float v) {  // lane n <-> n ^ 8 inside
 #ifndef TQ_WG_WAVES
 #define TQ_WG_WAVES 16
 #endif
-#ifndef TQ_AHEAD
-#define TQ_AHEAD 1
+#ifndef TQ_SPLIT
+#define TQ_SPLIT 0
 #endif
 constexpr int kMaxWaves = TQ_WG_WAVES;   // waves per workgroup (one workgroup per CU)
 constexpr int kWgThreads = 64 * kMaxWaves;
-constexpr int kAhead = TQ_AHEAD;         // stages of loads in flight
 
 // CONTIG: the workgroup holds every KV head, so a page is staged as the
 // contiguous bytes it is; else per-token chunk windows over the slice of the
@@ -227,55 +234,66 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     const int ri = isv ? r - nk : r;
     return (isv ? a.v_chunks : a.k_chunks) - ri * 64;
   };
-  uint32_t ld_src[MAXLD];
+  // Everything about a wave's loads but the block id is fixed for the whole
+  // walk: work it out once, in scalar registers that the compiler cannot
+  // re-derive from the kernel arguments inside the loop.
+  auto opaque = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  int ld_j[MAXLD], ld_pb[MAXLD], ld_soff[MAXLD], ld_dst[MAXLD];
+  uint32_t ld_lo[MAXLD], ld_hi[MAXLD];  // page pool base, as two scalar halves
+  uint32_t ld_voff[MAXLD];              // per-lane part of the source offset
+  bool ld_ok[MAXLD];                    // this lane carries a chunk
 #pragma unroll
-  for (int d = 0; d < MAXLD; ++d) ld_src[d] = CONTIG ? 0u : load_src(d);
-  // kAhead register sets: stage si lives in set si % kAhead
-  u32x4 stage_regs[kAhead][MAXLD];
-  auto issue_loads = [&](int si, auto set_tag) {  // global loads of stage si into registers
-    constexpr int SET = decltype(set_tag)::value;
+  for (int d = 0; d < MAXLD; ++d) {
+    const int x = wave + d * W;
+    const int r = x % nkv;
+    const bool isv = r >= nk;
+    const int ri = isv ? r - nk : r;
+    const uint8_t* pool = isv ? a.v_pages : a.k_pages;
+    ld_j[d] = opaque(x / nkv);
+    ld_pb[d] = opaque(isv ? v_rows : k_rows);
+    ld_lo[d] = (uint32_t)opaque((int)(uint32_t)(uintptr_t)pool);
+    ld_hi[d] = (uint32_t)opaque((int)(uint32_t)((uintptr_t)pool >> 32));
+    ld_soff[d] = CONTIG ? opaque(ri * 1024) : 0;
+    ld_voff[d] = CONTIG ? lane16 : load_src(d);
+    ld_dst[d] = opaque(kStages + (x / nkv) * a.page_slot_bytes + (isv ? a.k_region : 0) + ri * 1024);
+    ld_ok[d] = d < n_ld && lane < load_lanes(d);
+  }
+  const int stage_bytes = opaque(a.stage_bytes);
+  u32x4 stage_regs[MAXLD];
+  auto issue_loads = [&](int si) {  // global loads of stage si into registers
+    // Every wave issues exactly MAXLD loads, without branches, so that the
+    // compiler can count them and wait for one stage while later ones stay
+    // in flight.  A load that has no page (past the split's end, or beyond
+    // this wave's share) gets a zero-sized buffer: it returns zeros without
+    // touching memory, and write_stage skips it.  Lanes past the last chunk
+    // of a page fall outside the buffer in the same way.
 #pragma unroll
     for (int d = 0; d < MAXLD; ++d) {
-      // lanes and loads left out are left out of write_stage as well
-      if (d < n_ld) {
-        const int x = wave + d * W;
-        const int P = si * strm + x / nkv;
-        if (P < span) {
-          const bool isv = (x % nkv) >= nk;
-          const int blk = __builtin_amdgcn_readfirstlane(bt_lds[P]);
-          const uint8_t* base = isv ? a.v_pages + (int64_t)blk * a.v_page_bytes : a.k_pages + (int64_t)blk * a.k_page_bytes;
-          const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
-                                                                              isv ? v_rows : k_rows, 0x00020000);
-          const uint32_t src = CONTIG ? load_src(d) : ld_src[d];
-          if (lane < load_lanes(d))
-            stage_regs[SET][d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, src, 0, 0));
-        }
-      }
+      const int P = si * strm + ld_j[d];
+      const bool ok = d < n_ld && P < span;
+      const int blk = __builtin_amdgcn_readfirstlane(bt_lds[min(P, span - 1)]);
+      const uint64_t pool = ((uint64_t)ld_hi[d] << 32) | ld_lo[d];
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(pool) + (int64_t)blk * ld_pb[d];
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, ok ? ld_pb[d] : 0, 0x00020000);
+      stage_regs[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ld_voff[d], ld_soff[d], 0));
     }
   };
-  auto write_stage = [&](int si, int slot, auto set_tag) {  // the registers of stage si into LDS slot
-    constexpr int SET = decltype(set_tag)::value;
+  auto write_stage = [&](int si, int slot) {  // the registers of stage si into LDS slot
 #pragma unroll
     for (int d = 0; d < MAXLD; ++d) {
-      if (d < n_ld) {
-        const int x = wave + d * W;
-        const int j = x / nkv, r = x % nkv;
-        const bool isv = r >= nk;
-        const int ri = isv ? r - nk : r;
-        if (si * strm + j < span && lane < load_lanes(d)) {
-          const int off = kStages + slot * a.stage_bytes + j * a.page_slot_bytes + (isv ? a.k_region : 0) + ri * 1024;
-          *reinterpret_cast<u32x4*>(lds + off + 16 * lane) = stage_regs[SET][d];
-        }
-      }
+      if (d < n_ld && si * strm + ld_j[d] < span && ld_ok[d])
+        *reinterpret_cast<u32x4*>(lds + ld_dst[d] + slot * stage_bytes + 16 * lane) = stage_regs[d];
     }
   };
+
 
   // ---- rotated, scaled query as the B operand of the score MFMAs ----------
   // Lane (n, c) covers dims 32c..32c+31 (16 pairs); column n < 8 holds the
   // fp16 hi part of head n, column n + 8 its lo part.  MFMA m takes pairs
   // 2m and 2m+1, each twice (the A operand interleaves K hi and K lo).
   uint32_t qd[16];   // dword = fp16 pair (dims 2p, 2p+1) of this lane's column
-  float q_unscale;   // scores come out multiplied by 1 / q_unscale
+  float q_unscale;   // scores come out multiplied by 1 / q_unscale (one power of two per wave)
   {
     const bool has = hq < gsz;
     const int64_t qoff = ((int64_t)b * a.num_q_heads + qh0 + (has ? hq : 0)) * kHeadDim + 32 * c;
@@ -306,13 +324,18 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
       const float p = __shfl_xor(x[j], 32);
       x[j] = (c & 2) ? p - x[j] : x[j] + p;
     }
-    // power-of-two scale that puts the head's largest coordinate near 2^10,
+    // power-of-two scale that puts the wave's largest coordinate near 2^10,
     // so the fp16 hi/lo halves keep their precision for any query magnitude
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) amax = fmaxf(amax, __builtin_fabsf(x[j] * a.q_scale));
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    // one power of two for the whole wave (all its heads), so that it can
+    // be folded into the key norms
+    amax = max_across_rows(amax);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    amax = __builtin_amdgcn_readfirstlane(__float_as_int(amax)) == 0 ? 0.0f
+                                                                  : __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(amax)));
     int qe = 0;
     (void)__builtin_frexpf(amax, &qe);
     if (!(amax > 0.0f) || !(amax < __builtin_inff())) qe = 11;
@@ -338,6 +361,7 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0;
     int32_t* dst = reinterpret_cast<int32_t*>(lds + a.bt_base);
     for (int i = tid; i < span; i += 64 * W) dst[i] = bt[i];
+    if (tid < 16) reinterpret_cast<uint32_t*>(lds + kDecodeLdsBytes - 64)[tid] = 0u;
   }
   __syncthreads();
 
@@ -391,78 +415,97 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   float m_ref = -__builtin_inff();
   float l_part = 0.0f;
 
-  auto compute_page = [&](uint32_t pg, int tok0, auto full_tag) {
-    constexpr bool FULL = decltype(full_tag)::value;
+  // ---- one wave's page, in two parts ---------------------------------------------
+  // Key part: the key indices and table lookups (LDS), the score MFMAs, and
+  // the page's value index words and norms, all left in registers.  Value
+  // part: value table lookups, softmax, value MFMAs.  The stage loop runs a
+  // page's value part one iteration after its key part, which frees the
+  // page's stage slot a whole iteration early; half the waves of each SIMD
+  // run the two parts in the opposite order, so that the LDS-heavy key part
+  // of some waves overlaps the ALU-heavy value part of others.
+  constexpr int kVW = (VB == 3 || VB == 5) ? 2 : 1;  // value index words per token row slice
+  struct PagePart {
+    floatx4 sc;          // raw scores (fp16 hi and lo columns not yet summed)
+    uint32_t vw[kVW][4]; // value index words of tokens 4c .. 4c + 3
+    float nk, nv;        // the norms of token 4c + (n & 3)
+  };
+  auto key_part = [&](uint32_t pg, PagePart& o) {
     // pg: byte offset of the page slot inside the stage area
-    // -- keys: indices, norms, (hi, lo) fp16 pairs of 16 dim pairs, scores.
     uint32_t kw[KB];
 #pragma unroll
     for (int i = 0; i < KB; ++i) kw[i] = lds_u32(lds, pg + k_idx_off + 4 * i);
-    const float nk_mine = __uint_as_float(lds_u32(lds, pg + k_norm_off));
+    o.nk = __uint_as_float(lds_u32(lds, pg + k_norm_off));
     uint32_t kh[16], kl[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    auto klook = [&](int k) {
       const u32x2 e = *reinterpret_cast<const u32x2*>(k_tab + pair_addr<KB>(kw, k, k_lane));
       kh[k] = e[0];
       kl[k] = e[1];
-    }
+    };
     // A = [K_hi(p), K_lo(p), K_hi(p'), K_lo(p')], B = [q(p), q(p), q(p'), q(p')]
     floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    auto kmfma = [&](int m) {
       const half8 A = __builtin_bit_cast(half8, u32x4{kh[2 * m], kl[2 * m], kh[2 * m + 1], kl[2 * m + 1]});
       const half8 Bq = __builtin_bit_cast(half8, u32x4{qd[2 * m], qd[2 * m], qd[2 * m + 1], qd[2 * m + 1]});
       sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq, sc, 0, 0, 0);
+    };
+    // rolling window: the lookups of the next two MFMAs are in flight while
+    // one runs, which keeps few lookup results live at a time
+    constexpr int kWin = 2;
+#pragma unroll
+    for (int k = 0; k < 2 * kWin; ++k) klook(k);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      if (m + kWin < 8) {
+        klook(2 * (m + kWin));
+        klook(2 * (m + kWin) + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      kmfma(m);
     }
-    // keep the value-side reads below the key side (register pressure)
-    __builtin_amdgcn_sched_barrier(0);
-    // -- values: norms, indices, and the lookups: dword (V[t][2p], V[t][2p+1])
-    // for pair p = 4n + blk of token 4c + j is exactly A[row n][k = 2j, 2j+1]
-    // of value block blk
-    const float nv_mine = __uint_as_float(lds_u32(lds, pg + v_norm_off));
-    uint32_t vw[4], vw2[4];
+    o.sc = sc;
+    // value norms and index words: the slot is rewritten before the value part runs
+    o.nv = __uint_as_float(lds_u32(lds, pg + v_norm_off));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t vo = pg + v_dat_at(r);
       if constexpr (VB == 2) {
-        vw[r] = *reinterpret_cast<const uint16_t*>(lds + vo);
+        o.vw[0][r] = *reinterpret_cast<const uint16_t*>(lds + vo);
       } else {
-        vw[r] = lds_u32(lds, vo);
-        if constexpr (VB == 3 || VB == 5) vw2[r] = lds_u32(lds, vo + 4);
+        o.vw[0][r] = lds_u32(lds, vo);
+        if constexpr (kVW == 2) o.vw[kVW - 1][r] = lds_u32(lds, vo + 4);
       }
     }
+  };
+  auto value_part = [&](const PagePart& o, int tok0, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    // -- value lookups: dword (V[t][2p], V[t][2p+1]) for pair p = 4n + blk of
+    // token 4c + j is exactly A[row n][k = 2j, 2j+1] of value block blk
     uint32_t va[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t words[2];
-      if constexpr (VB == 3 || VB == 5) {
-        const uint64_t all = ((((uint64_t)vw2[j]) << 32) | vw[j]) >> v_shift;
+      if constexpr (kVW == 2) {
+        const uint64_t all = ((((uint64_t)o.vw[kVW - 1][j]) << 32) | o.vw[0][j]) >> v_shift;
         words[0] = (uint32_t)all;
         words[1] = (uint32_t)(all >> 32);
       } else {
-        words[0] = vw[j];
+        words[0] = o.vw[0][j];
         words[1] = 0;
       }
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) va[blk][j] = lds_u32(v_tab, pair_addr<VB>(words, blk, v_lane));
     }
-    float nk[4], nv[4];
-    nk[0] = quad_bcast<0>(nk_mine);
-    nk[1] = quad_bcast<1>(nk_mine);
-    nk[2] = quad_bcast<2>(nk_mine);
-    nk[3] = quad_bcast<3>(nk_mine);
-    nv[0] = quad_bcast<0>(nv_mine);
-    nv[1] = quad_bcast<1>(nv_mine);
-    nv[2] = quad_bcast<2>(nv_mine);
-    nv[3] = quad_bcast<3>(nv_mine);
     // -- softmax bookkeeping (log2 domain).  e = an upper bound of log2(n_v)
-    // from the exponent bits (clamped so empty rows cannot blow up p).
+    // from the exponent bits (clamped so empty rows cannot blow up p).  The
+    // per-token factors are formed on the lane that read the norm and
+    // broadcast inside each quad (lane (n, c) needs tokens 4c .. 4c + 3).
+    const float nkq_mine = o.nk * q_unscale;
+    const float e_mine = fmaxf(__builtin_fmaf((float)(__float_as_uint(o.nv) >> 24), 2.0f, -126.0f), -64.0f);
     float full[4], xv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      full[r] = (sc[r] + row_ror8(sc[r])) * (nk[r] * q_unscale);
-      const float e = fmaxf(__builtin_fmaf((float)(__float_as_uint(nv[r]) >> 24), 2.0f, -126.0f), -64.0f);
-      xv[r] = full[r] + e;
+      full[r] = (o.sc[r] + row_ror8(o.sc[r])) * quad_bcast_r(nkq_mine, r);
+      xv[r] = full[r] + quad_bcast_r(e_mine, r);
       if constexpr (!FULL) xv[r] = (tok0 + r < L) ? xv[r] : -__builtin_inff();
     }
     float pmax = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
@@ -482,7 +525,7 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
       float pr = __builtin_amdgcn_exp2f(full[r] - m_ref);
       if constexpr (!FULL) pr = (tok0 + r < L) ? pr : 0.0f;
       l_part += pr;
-      float wv = pr * nv[r];
+      float wv = pr * quad_bcast_r(o.nv, r);
       if constexpr (!FULL) wv = (tok0 + r < L) ? wv : 0.0f;  // rows past the end may hold anything
       const _Float16 hi = (_Float16)wv;
       const _Float16 lo = (_Float16)(wv - (float)hi);
@@ -503,36 +546,81 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   // ---- stage loop ------------------------------------------------------------------
   // Iteration i: barrier (stage i is in slot i & 1 for everyone, and every
   // wave is done with slot (i + 1) & 1), store stage i + 1 from its
-  // registers into that slot, issue the loads of stage i + 1 + kAhead into
-  // the same registers, compute this wave's page of stage i.  kAhead stages
-  // of loads are in flight during the compute.
+  // registers into that slot, issue the loads of stage i + 2 into the same
+  // registers, then the key part of this wave's page of stage i and the
+  // value part of its page of stage i - 1 (in either order).
   const int nit = (span + strm - 1) / strm;
-  using Set0 = std::integral_constant<int, 0>;
-  issue_loads(0, Set0{});
-  write_stage(0, 0, Set0{});
-  [&]<int... U>(std::integer_sequence<int, U...>) {
-    (issue_loads(1 + U, std::integral_constant<int, (1 + U) % kAhead>{}), ...);
-  }(std::make_integer_sequence<int, kAhead>{});
-  auto iteration = [&](int i, auto full_tag, auto set_tag) {  // set_tag: (i + 1) % kAhead
+  issue_loads(0);
+  write_stage(0, 0);
+  issue_loads(1);
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+#if TQ_SPLIT
+  const bool value_first = ((wave >> 2) & 1) != 0;  // waves w, w + 4, w + 8, w + 12 share a SIMD
+  PagePart part[2];
+  auto iteration = [&](int i, auto cur_tag) {  // cur_tag: i & 1
+    constexpr int CUR = decltype(cur_tag)::value;
     __syncthreads();
-    write_stage(i + 1, (i + 1) & 1, set_tag);
-    issue_loads(i + 1 + kAhead, set_tag);
+    write_stage(i + 1, (i + 1) & 1);
+    issue_loads(i + 2);
     const int P = strm * i + st;
-    if (P < span)
-      compute_page((uint32_t)((i & 1) * a.stage_bytes + st * a.page_slot_bytes), (p0 + P) * kBlockSize + 4 * c,
-                   full_tag);
+    const uint32_t pg = (uint32_t)((i & 1) * stage_bytes + st * a.page_slot_bytes);
+    const bool prev = i > 0 && P - strm < span;  // only the sequence's last page is partial: not this one
+    // (scheduling barriers keep the compiler from interleaving the two
+    // parts, which would hold both parts' lookups in registers at once)
+    if (value_first) {
+      if (prev) value_part(part[CUR ^ 1], 0, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      if (P < span) key_part(pg, part[CUR]);
+    } else {
+      if (P < span) key_part(pg, part[CUR]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (prev) value_part(part[CUR ^ 1], 0, std::true_type{});
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int i0 = 0;
+  for (; i0 + 2 < nit; i0 += 2) {  // two iterations without branches between their loads
+    iteration(i0, C0{});
+    iteration(i0 + 1, C1{});
+  }
+  if (nit - i0 == 2) {
+    iteration(i0, C0{});
+    iteration(i0 + 1, C1{});
+  } else {
+    iteration(i0, C0{});
+  }
+  {  // the value part of the last iteration's page, masked at the sequence's end
+    const int P = strm * (nit - 1) + st;
+    if (P < span) {
+      const int tok0 = (p0 + P) * kBlockSize + 4 * c;
+      if ((nit - 1) & 1)
+        value_part(part[1], tok0, std::false_type{});
+      else
+        value_part(part[0], tok0, std::false_type{});
+    }
+  }
+#else
+  auto iteration = [&](int i, auto full_tag) {
+    __syncthreads();
+    write_stage(i + 1, (i + 1) & 1);
+    issue_loads(i + 2);
+    const int P = strm * i + st;
+    if (P < span) {
+      PagePart part;
+      key_part((uint32_t)((i & 1) * stage_bytes + st * a.page_slot_bytes), part);
+      // keep the value-side lookups below the key side (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
+      value_part(part, (p0 + P) * kBlockSize + 4 * c, full_tag);
+    }
   };
   // only the sequence's last page can be partial, and it is in the last
   // iteration: the others skip the masking
-  for (int i0 = 0; i0 + 1 < nit; i0 += kAhead) {
-    [&]<int... U>(std::integer_sequence<int, U...>) {
-      ((i0 + U + 1 < nit ? iteration(i0 + U, std::true_type{}, std::integral_constant<int, (U + 1) % kAhead>{})
-                         : void()), ...);
-    }(std::make_integer_sequence<int, kAhead>{});
-  }
-  [&]<int... U>(std::integer_sequence<int, U...>) {
-    ((nit % kAhead == U ? iteration(nit - 1, std::false_type{}, std::integral_constant<int, U>{}) : void()), ...);
-  }(std::make_integer_sequence<int, kAhead>{});
+  for (int i = 0; i + 1 < nit; ++i) iteration(i, std::true_type{});
+  iteration(nit - 1, std::false_type{});
+  (void)C0{};
+  (void)C1{};
+#endif
 
   // ---- finish the split ---------------------------------------------------------
   float l_tot = l_part + __shfl_xor(l_part, 16);
