@@ -119,7 +119,7 @@ def main():
     ap.add_argument("--config", default="long_context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-flush", action="store_true", help="skip the 1 GiB cache flush before each timed decode")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush (1 GiB write, then 1 GiB read) before each timed step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -165,13 +165,19 @@ def main():
     del kraw_d, vraw_d
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    # writing 1 GiB before each timed decode evicts the pages from L2 and the 256 MB MALL
+    # Before each timed step, untimed: write 1 GiB (evicts the pages from L2
+    # and the 256 MB MALL), then read another 1 GiB.  The read pass makes the
+    # caches write back the memset's dirty lines before the timed region;
+    # without it that write-back (up to the MALL's 256 MB) lands inside the
+    # decode and is charged to it.
     flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_rd = None if args.no_flush else torch.ones(1 << 27, dtype=torch.int64, device=dev)
 
     def step(i=None):
         # timed: the row writer for the new token of every sequence, then the decode
         if flush is not None:
             flush.zero_()
+            flush_rd.sum()
         if i is not None:
             ev[i][0].record()
         api.write_kv(ctx, k_new, kp, new_slots, w.k_bits, err_count=err, check_slots=False)

@@ -134,15 +134,27 @@ __device__ __forceinline__ float row_ror8(float v) {  // lane n <-> n ^ 8 inside
 #ifndef TQ_WG_WAVES
 #define TQ_WG_WAVES 16
 #endif
-#ifndef TQ_SPLIT
-#define TQ_SPLIT 0
-#endif
 constexpr int kMaxWaves = TQ_WG_WAVES;   // waves per workgroup (one workgroup per CU)
 constexpr int kWgThreads = 64 * kMaxWaves;
 
 // CONTIG: the workgroup holds every KV head, so a page is staged as the
 // contiguous bytes it is; else per-token chunk windows over the slice of the
 // workgroup's heads.  MAXLD: 1 KB loads per wave per stage.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// One buffer_load_dwordx4 with the lds modifier moves 64 16-byte chunks
+// from global memory into LDS at M0 + 16 * lane without passing through
+// registers.  It is inline assembly so that the compiler does not make the
+// LDS reads of other slots wait for it; the kernel waits itself.
+__device__ __forceinline__ void copy_chunk_to_lds(i32x4 rsrc, uint32_t lds_addr, uint32_t voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int KB, int VB, bool CONTIG, int MAXLD>
 __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) {
   // all of the CU's LDS, statically: addresses are then known constants
@@ -150,6 +162,9 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   using KT = PairTable<KB>;
   using VT = PairTable<VB>;
   constexpr bool kShareV = (KB == VB);
+  // run a page's value part one iteration after its key part (registers allow it
+  // when a value index word per token row slice suffices)
+  constexpr bool kSplit = (VB == 2 || VB == 4) && CONTIG && MAXLD == 3;
   // LDS: lookup tables at 0 (so their addresses need no base), then two
   // stage slots, then the split's block ids
   constexpr int kVTab = 0;
@@ -259,31 +274,26 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     ld_ok[d] = d < n_ld && lane < load_lanes(d);
   }
   const int stage_bytes = opaque(a.stage_bytes);
-  u32x4 stage_regs[MAXLD];
-  auto issue_loads = [&](int si) {  // global loads of stage si into registers
-    // Every wave issues exactly MAXLD loads, without branches, so that the
-    // compiler can count them and wait for one stage while later ones stay
-    // in flight.  A load that has no page (past the split's end, or beyond
-    // this wave's share) gets a zero-sized buffer: it returns zeros without
-    // touching memory, and write_stage skips it.  Lanes past the last chunk
-    // of a page fall outside the buffer in the same way.
+  // stage si straight into LDS slot `slot` (no registers): the destination
+  // slot must be free when this is issued, and the data is there once this
+  // wave has waited for its vector memory counter and the workgroup has met
+  // at a barrier
+  auto issue_dma = [&](int si, int slot) {
 #pragma unroll
     for (int d = 0; d < MAXLD; ++d) {
       const int P = si * strm + ld_j[d];
-      const bool ok = d < n_ld && P < span;
-      const int blk = __builtin_amdgcn_readfirstlane(bt_lds[min(P, span - 1)]);
-      const uint64_t pool = ((uint64_t)ld_hi[d] << 32) | ld_lo[d];
-      const uint8_t* base = reinterpret_cast<const uint8_t*>(pool) + (int64_t)blk * ld_pb[d];
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, ok ? ld_pb[d] : 0, 0x00020000);
-      stage_regs[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ld_voff[d], ld_soff[d], 0));
-    }
-  };
-  auto write_stage = [&](int si, int slot) {  // the registers of stage si into LDS slot
-#pragma unroll
-    for (int d = 0; d < MAXLD; ++d) {
-      if (d < n_ld && si * strm + ld_j[d] < span && ld_ok[d])
-        *reinterpret_cast<u32x4*>(lds + ld_dst[d] + slot * stage_bytes + 16 * lane) = stage_regs[d];
+      if (d < n_ld && P < span) {
+        const int blk = __builtin_amdgcn_readfirstlane(bt_lds[P]);
+        const uint64_t pool = ((uint64_t)ld_hi[d] << 32) | ld_lo[d];
+        const uint64_t base = pool + (uint64_t)((int64_t)blk * ld_pb[d]);
+        i32x4 rs;
+        rs.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+        rs.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu));
+        rs.z = ld_pb[d];
+        rs.w = 0x00020000;
+        const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ld_dst[d] + slot * stage_bytes));
+        if (ld_ok[d]) copy_chunk_to_lds(rs, dst, ld_voff[d], ld_soff[d]);
+      }
     }
   };
 
@@ -544,83 +554,83 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   };
 
   // ---- stage loop ------------------------------------------------------------------
-  // Iteration i: barrier (stage i is in slot i & 1 for everyone, and every
-  // wave is done with slot (i + 1) & 1), store stage i + 1 from its
-  // registers into that slot, issue the loads of stage i + 2 into the same
-  // registers, then the key part of this wave's page of stage i and the
-  // value part of its page of stage i - 1 (in either order).
+  // Stage i lives in LDS slot i & 1.  Iteration i: wait for this wave's
+  // copies of stage i, barrier (now every wave's copies are in, and every
+  // wave is done with stage i - 1), start the copies of stage i + 1 into the
+  // other slot, then compute.  The copies of one stage are in flight while
+  // the previous one is computed.
   const int nit = (span + strm - 1) / strm;
-  issue_loads(0);
-  write_stage(0, 0);
-  issue_loads(1);
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-#if TQ_SPLIT
-  const bool value_first = ((wave >> 2) & 1) != 0;  // waves w, w + 4, w + 8, w + 12 share a SIMD
-  PagePart part[2];
-  auto iteration = [&](int i, auto cur_tag) {  // cur_tag: i & 1
-    constexpr int CUR = decltype(cur_tag)::value;
+  auto advance = [&](int i) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    write_stage(i + 1, (i + 1) & 1);
-    issue_loads(i + 2);
-    const int P = strm * i + st;
-    const uint32_t pg = (uint32_t)((i & 1) * stage_bytes + st * a.page_slot_bytes);
-    const bool prev = i > 0 && P - strm < span;  // only the sequence's last page is partial: not this one
-    // (scheduling barriers keep the compiler from interleaving the two
-    // parts, which would hold both parts' lookups in registers at once)
-    if (value_first) {
-      if (prev) value_part(part[CUR ^ 1], 0, std::true_type{});
+    issue_dma(i + 1, (i + 1) & 1);
+  };
+  auto slot_of = [&](int i) { return (uint32_t)((i & 1) * stage_bytes + st * a.page_slot_bytes); };
+  issue_dma(0, 0);
+  if constexpr (kSplit) {
+    // Iteration i runs the value part of this wave's page of stage i - 1,
+    // then the key part of its page of stage i.  The value part needs no
+    // stage data, so it starts right after the barrier; the key part reads
+    // the slot.  Iterations 1 .. nit - 2 have both pages whole, so their
+    // bodies have no branches.  (The scheduling barriers keep the compiler
+    // from interleaving the two parts, which would hold both parts' lookups
+    // in registers at once.)
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    PagePart part[2];  // part[i & 1]: this wave's page of stage i
+    auto iteration = [&](int i, auto cur_tag) {  // cur_tag: i & 1
+      constexpr int CUR = decltype(cur_tag)::value;
+      advance(i);
+      value_part(part[CUR ^ 1], 0, std::true_type{});
       __builtin_amdgcn_sched_barrier(0);
-      if (P < span) key_part(pg, part[CUR]);
-    } else {
-      if (P < span) key_part(pg, part[CUR]);
+      key_part(slot_of(i), part[CUR]);
       __builtin_amdgcn_sched_barrier(0);
-      if (prev) value_part(part[CUR ^ 1], 0, std::true_type{});
-    }
+    };
+    // the last iteration (i >= 1), then the value part of its page, masked
+    // at the sequence's end (only the sequence's last page can be partial)
+    auto last = [&](int i, auto cur_tag) {
+      constexpr int CUR = decltype(cur_tag)::value;
+      const int P = strm * i + st;
+      if (i > 0) {
+        advance(i);
+        value_part(part[CUR ^ 1], 0, std::true_type{});
+        if (P < span) key_part(slot_of(i), part[CUR]);
+      }
+      if (P < span) value_part(part[CUR], (p0 + P) * kBlockSize + 4 * c, std::false_type{});
+    };
+    advance(0);  // iteration 0: a key part only
+    if (st < span) key_part(slot_of(0), part[0]);
     __builtin_amdgcn_sched_barrier(0);
-  };
-  int i0 = 0;
-  for (; i0 + 2 < nit; i0 += 2) {  // two iterations without branches between their loads
-    iteration(i0, C0{});
-    iteration(i0 + 1, C1{});
-  }
-  if (nit - i0 == 2) {
-    iteration(i0, C0{});
-    iteration(i0 + 1, C1{});
+    int i = 1;
+    for (; i + 1 < nit - 1; i += 2) {
+      iteration(i, C1{});
+      iteration(i + 1, C0{});
+    }
+    if (i < nit - 1) {
+      iteration(i, C1{});
+      ++i;
+    }
+    if (nit == 1)
+      last(0, C0{});
+    else if (i & 1)
+      last(i, C1{});
+    else
+      last(i, C0{});
   } else {
-    iteration(i0, C0{});
+    // both parts of a page in its own iteration (fewer registers live)
+    auto iteration = [&](int i, auto full_tag) {
+      advance(i);
+      const int P = strm * i + st;
+      if (P < span) {
+        PagePart part;
+        key_part(slot_of(i), part);
+        __builtin_amdgcn_sched_barrier(0);
+        value_part(part, (p0 + P) * kBlockSize + 4 * c, full_tag);
+      }
+    };
+    for (int i = 0; i + 1 < nit; ++i) iteration(i, std::true_type{});
+    iteration(nit - 1, std::false_type{});
   }
-  {  // the value part of the last iteration's page, masked at the sequence's end
-    const int P = strm * (nit - 1) + st;
-    if (P < span) {
-      const int tok0 = (p0 + P) * kBlockSize + 4 * c;
-      if ((nit - 1) & 1)
-        value_part(part[1], tok0, std::false_type{});
-      else
-        value_part(part[0], tok0, std::false_type{});
-    }
-  }
-#else
-  auto iteration = [&](int i, auto full_tag) {
-    __syncthreads();
-    write_stage(i + 1, (i + 1) & 1);
-    issue_loads(i + 2);
-    const int P = strm * i + st;
-    if (P < span) {
-      PagePart part;
-      key_part((uint32_t)((i & 1) * stage_bytes + st * a.page_slot_bytes), part);
-      // keep the value-side lookups below the key side (register pressure)
-      __builtin_amdgcn_sched_barrier(0);
-      value_part(part, (p0 + P) * kBlockSize + 4 * c, full_tag);
-    }
-  };
-  // only the sequence's last page can be partial, and it is in the last
-  // iteration: the others skip the masking
-  for (int i = 0; i + 1 < nit; ++i) iteration(i, std::true_type{});
-  iteration(nit - 1, std::false_type{});
-  (void)C0{};
-  (void)C1{};
-#endif
 
   // ---- finish the split ---------------------------------------------------------
   float l_tot = l_part + __shfl_xor(l_part, 16);
