@@ -207,8 +207,13 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   // ---- staging geometry --------------------------------------------------------
   // A stage is strm consecutive pages (one per stream) of the workgroup's
   // heads; two stage slots alternate.  A page slot holds the K part, then the
-  // V part.  CONTIG: each part is the page's bytes as they are (token t of
-  // head g at t * Hkv * RB + g * RB).  Else the slice of the workgroup's heads
+  // V part.  CONTIG: each row (token t, head g) gets a slice of H = 16 hs
+  // bytes at t * 16 tc + g * H, where hs = ceil(RB / 16) and tc (odd) is
+  // the 16-byte chunks per token: slices start 16-byte aligned and token
+  // rows start on different bank groups, so the lanes of a wave (one token
+  // each) read their rows without bank conflicts.  A slice holds the row's
+  // bytes 0 .. H - 17 in place and its last 16 bytes (ending with the norm)
+  // in its last chunk, so the norm sits at H - 4.  Else the slice of the workgroup's heads
   // for token t (kv_per_wg * RB bytes) is staged as the C 16-byte chunks of a
   // window that covers it and starts delta_t (at most 31) bytes before it:
   // token t at t * 16C + delta_t.
@@ -226,14 +231,20 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   // else V.  Wave w issues loads w, w + W, ... (at most MAXLD).
   const int nk = a.k_loads, nkv = a.k_loads + a.v_loads;
   const int n_ld = strm * nkv > wave ? (strm * nkv - wave + W - 1) / W : 0;
-  const uint32_t lane16 = 16u * (uint32_t)lane;
   auto load_src = [&](int d) -> uint32_t {  // lane's source offset inside the page
     const int x = wave + d * W;
     const int r = x % nkv;
     const bool isv = r >= nk;
     const int ri = isv ? r - nk : r;
     if constexpr (CONTIG) {
-      return (uint32_t)(ri * 1024) + lane16;
+      const int tc = isv ? vC : kC, hs = isv ? a.v_slice_chunks : a.k_slice_chunks;
+      const int RB = isv ? a.v_row_bytes : a.k_row_bytes;
+      const int q = ri * 64 + lane;  // the LDS chunk this lane fills
+      const int t = q / tc;
+      const int rem = q - t * tc;
+      const int gg = min(rem / hs, a.num_kv_heads - 1);  // (padding chunks: any row, not stored)
+      const int j = rem - (rem / hs) * hs;
+      return (uint32_t)((t * a.num_kv_heads + gg) * RB + (j == hs - 1 ? RB - 16 : 16 * j));
     } else {
       const int C = isv ? vC : kC;
       const int ch = min(ri * 64 + lane, kBlockSize * C - 1);
@@ -242,12 +253,18 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
       return (uint32_t)(window(t, isv ? a.v_row_bytes : a.k_row_bytes, C, isv ? v_rows : k_rows, dl) + 16 * (ch - t * C));
     }
   };
-  auto load_lanes = [&](int d) {  // lanes below this carry a chunk
+  auto lane_loads = [&](int d) {  // this lane carries a chunk of load d
     const int x = wave + d * W;
     const int r = x % nkv;
     const bool isv = r >= nk;
     const int ri = isv ? r - nk : r;
-    return (isv ? a.v_chunks : a.k_chunks) - ri * 64;
+    const int q = ri * 64 + lane;
+    if (q >= (isv ? a.v_chunks : a.k_chunks)) return false;
+    if constexpr (CONTIG) {  // not a token row's padding chunk
+      const int tc = isv ? vC : kC;
+      return q - (q / tc) * tc < a.num_kv_heads * (isv ? a.v_slice_chunks : a.k_slice_chunks);
+    }
+    return true;
   };
   // Everything about a wave's loads but the block id is fixed for the whole
   // walk: work it out once, in scalar registers that the compiler cannot
@@ -268,10 +285,10 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     ld_pb[d] = opaque(isv ? v_rows : k_rows);
     ld_lo[d] = (uint32_t)opaque((int)(uint32_t)(uintptr_t)pool);
     ld_hi[d] = (uint32_t)opaque((int)(uint32_t)((uintptr_t)pool >> 32));
-    ld_soff[d] = CONTIG ? opaque(ri * 1024) : 0;
-    ld_voff[d] = CONTIG ? lane16 : load_src(d);
+    ld_soff[d] = 0;
+    ld_voff[d] = load_src(d);
     ld_dst[d] = opaque(kStages + (x / nkv) * a.page_slot_bytes + (isv ? a.k_region : 0) + ri * 1024);
-    ld_ok[d] = d < n_ld && lane < load_lanes(d);
+    ld_ok[d] = d < n_ld && lane_loads(d);
   }
   const int stage_bytes = opaque(a.stage_bytes);
   // stage si straight into LDS slot `slot` (no registers): the destination
@@ -378,7 +395,7 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   // ---- per-lane LDS offsets inside a page slot ------------------------------------
   auto tok_k = [&](int t) {
     if constexpr (CONTIG) {
-      return t * a.num_kv_heads * a.k_row_bytes + g * a.k_row_bytes;
+      return 16 * (t * kC + g * a.k_slice_chunks);
     } else {
       int d;
       (void)window(t, a.k_row_bytes, kC, k_rows, d);
@@ -387,7 +404,7 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   };
   auto tok_v = [&](int t) {
     if constexpr (CONTIG) {
-      return a.k_region + t * a.num_kv_heads * a.v_row_bytes + g * a.v_row_bytes;
+      return a.k_region + 16 * (t * vC + g * a.v_slice_chunks);
     } else {
       int d;
       (void)window(t, a.v_row_bytes, vC, v_rows, d);
@@ -399,10 +416,12 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   const uint32_t k_idx_off = (uint32_t)(kStages + tok_k(n) + 4 * KB * c);
   // each lane reads the norms of token 4c + (n & 3); quad broadcasts hand
   // every lane those of tokens 4c .. 4c + 3
-  const uint32_t k_norm_off = (uint32_t)(kStages + tok_k(4 * c + (n & 3)) + a.k_row_bytes - 4);
-  const uint32_t v_norm_off = (uint32_t)(kStages + tok_v(4 * c + (n & 3)) + a.v_row_bytes - 4);
+  const int k_norm_at = CONTIG ? 16 * a.k_slice_chunks - 4 : a.k_row_bytes - 4;
+  const int v_norm_at = CONTIG ? 16 * a.v_slice_chunks - 4 : a.v_row_bytes - 4;
+  const uint32_t k_norm_off = (uint32_t)(kStages + tok_k(4 * c + (n & 3)) + k_norm_at);
+  const uint32_t v_norm_off = (uint32_t)(kStages + tok_v(4 * c + (n & 3)) + v_norm_at);
   // value bytes of token 4c + r: CONTIG: base + r * token stride
-  const int v_tstride = a.num_kv_heads * a.v_row_bytes;
+  const int v_tstride = 16 * vC;
   uint32_t v_dat_off[CONTIG ? 1 : 4];
 #pragma unroll
   for (int r = 0; r < (CONTIG ? 1 : 4); ++r) v_dat_off[r] = (uint32_t)(kStages + tok_v(4 * c + r) + v_dat);
@@ -442,8 +461,14 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   auto key_part = [&](uint32_t pg, PagePart& o) {
     // pg: byte offset of the page slot inside the stage area
     uint32_t kw[KB];
+    if constexpr (CONTIG && KB == 4) {  // 16-byte aligned: one read
+      const u32x4 w4 = *reinterpret_cast<const u32x4*>(lds + pg + k_idx_off);
 #pragma unroll
-    for (int i = 0; i < KB; ++i) kw[i] = lds_u32(lds, pg + k_idx_off + 4 * i);
+      for (int i = 0; i < 4; ++i) kw[i] = w4[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < KB; ++i) kw[i] = lds_u32(lds, pg + k_idx_off + 4 * i);
+    }
     o.nk = __uint_as_float(lds_u32(lds, pg + k_norm_off));
     uint32_t kh[16], kl[16];
     auto klook = [&](int k) {

@@ -238,6 +238,7 @@ struct SplitPlan {
   int pages_per_split;
   int num_splits;
   int tok_chunks[2];  // K, V
+  int slice_chunks[2];
   int chunks[2];
   int loads[2];
   int page_slot;
@@ -264,10 +265,12 @@ bool plan_split(int batch, int num_kv_heads, int group, int max_seq_len, int k_b
   for (int kv = num_kv_heads; kv >= 1 && !found; --kv) {
     if (num_kv_heads % kv || kv * p.q_groups > kMaxWavesPerWg) continue;
     for (int i = 0; i < 2; ++i) {
-      if (kv == num_kv_heads) {  // whole pages, as they are
-        p.tok_chunks[i] = 0;
-        p.chunks[i] = num_kv_heads * rb[i];  // 16 * Hkv * RB / 16
-      } else {                   // window start at most 31 bytes before the slice
+      if (kv == num_kv_heads) {  // whole pages: rows in 16-byte slices, an odd number of chunks per token
+        p.slice_chunks[i] = (rb[i] + 15) / 16;
+        p.tok_chunks[i] = num_kv_heads * p.slice_chunks[i] | 1;
+        p.chunks[i] = tq::kBlockSize * p.tok_chunks[i];
+      } else {
+        p.slice_chunks[i] = 0;                   // window start at most 31 bytes before the slice
         p.tok_chunks[i] = (kv * rb[i] + 16 + 15) / 16;
         p.chunks[i] = tq::kBlockSize * p.tok_chunks[i];
       }
@@ -488,6 +491,8 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   d.q_dtype = (int)q_dtype;
   d.k_tok_chunks = p.tok_chunks[0];
   d.v_tok_chunks = p.tok_chunks[1];
+  d.k_slice_chunks = p.slice_chunks[0];
+  d.v_slice_chunks = p.slice_chunks[1];
   d.k_chunks = p.chunks[0];
   d.v_chunks = p.chunks[1];
   d.k_loads = p.loads[0];

@@ -59,9 +59,11 @@ struct DecodeArgs {
   int32_t pages_per_split;       // pages per workgroup
   int32_t num_splits;            // S
   int32_t q_dtype;               // tq_dtype of q
-  // staging (per component): whole pages when kv_per_wg == num_kv_heads,
-  // else a token's slice of the workgroup's heads as C 16-byte chunks
-  int32_t k_tok_chunks, v_tok_chunks;  // C (slices only)
+  // staging (per component): whole pages when kv_per_wg == num_kv_heads
+  // (each row in a 16-byte aligned slice, token rows of an odd number of
+  // chunks), else a token's slice of the workgroup's heads as C 16-byte chunks
+  int32_t k_tok_chunks, v_tok_chunks;  // 16-byte chunks per token row: C (slices) or tc (whole pages)
+  int32_t k_slice_chunks, v_slice_chunks;  // whole pages: chunks per (token, head) slice, ceil(RB / 16)
   int32_t k_chunks, v_chunks;    // 16-byte chunks per page
   int32_t k_loads, v_loads;      // 1 KB loads per page: ceil(chunks / 64)
   int32_t k_region;              // LDS bytes of a page's K part: 16 k_chunks
