@@ -537,11 +537,16 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     const float nkq_mine = o.nk * q_unscale;
     const float e_mine = fmaxf(__builtin_fmaf((float)(__float_as_uint(o.nv) >> 24), 2.0f, -126.0f), -64.0f);
     float full[4], xv[4];
+    {
+      // (no contraction here: a plain multiply and add each take their
+      // broadcast operand straight from the neighbouring lane)
+#pragma clang fp contract(off)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      full[r] = (o.sc[r] + row_ror8(o.sc[r])) * quad_bcast_r(nkq_mine, r);
-      xv[r] = full[r] + quad_bcast_r(e_mine, r);
-      if constexpr (!FULL) xv[r] = (tok0 + r < L) ? xv[r] : -__builtin_inff();
+      for (int r = 0; r < 4; ++r) {
+        full[r] = (o.sc[r] + row_ror8(o.sc[r])) * quad_bcast_r(nkq_mine, r);
+        xv[r] = full[r] + quad_bcast_r(e_mine, r);
+        if constexpr (!FULL) xv[r] = (tok0 + r < L) ? xv[r] : -__builtin_inff();
+      }
     }
     float pmax = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
     pmax = max_across_rows(pmax);
