@@ -607,8 +607,10 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     // in registers at once.)
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
-    PagePart part[2];  // part[i & 1]: this wave's page of stage i
-    auto iteration = [&](int i, auto cur_tag) {  // cur_tag: i & 1
+    // part[(nit - 1 - i) & 1]: this wave's page of stage i (so that the last
+    // iteration always fills part[0] and a single copy of the tail exists)
+    PagePart part[2];
+    auto iteration = [&](int i, auto cur_tag) {  // cur_tag: (nit - 1 - i) & 1
       constexpr int CUR = decltype(cur_tag)::value;
       advance(i);
       value_part(part[CUR ^ 1], 0, std::true_type{});
@@ -616,36 +618,35 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
       key_part(slot_of(i), part[CUR]);
       __builtin_amdgcn_sched_barrier(0);
     };
-    // the last iteration (i >= 1), then the value part of its page, masked
-    // at the sequence's end (only the sequence's last page can be partial)
-    auto last = [&](int i, auto cur_tag) {
-      constexpr int CUR = decltype(cur_tag)::value;
-      const int P = strm * i + st;
-      if (i > 0) {
-        advance(i);
-        value_part(part[CUR ^ 1], 0, std::true_type{});
-        if (P < span) key_part(slot_of(i), part[CUR]);
-      }
-      if (P < span) value_part(part[CUR], (p0 + P) * kBlockSize + 4 * c, std::false_type{});
-    };
-    advance(0);  // iteration 0: a key part only
-    if (st < span) key_part(slot_of(0), part[0]);
+    // iteration 0: a key part only
+    advance(0);
+    if (st < span) {
+      if ((nit - 1) & 1)
+        key_part(slot_of(0), part[1]);
+      else
+        key_part(slot_of(0), part[0]);
+    }
     __builtin_amdgcn_sched_barrier(0);
+    // iterations 1 .. nit - 2 (both pages whole) in pairs that end with
+    // iteration nit - 2, whose page is in part 1
     int i = 1;
-    for (; i + 1 < nit - 1; i += 2) {
-      iteration(i, C1{});
-      iteration(i + 1, C0{});
+    if (nit - 2 > 0 && ((nit - 2) & 1)) iteration(i++, C1{});
+    for (; i < nit - 1; i += 2) {
+      iteration(i, C0{});
+      iteration(i + 1, C1{});
     }
-    if (i < nit - 1) {
-      iteration(i, C1{});
-      ++i;
+    // the last iteration (if it is not iteration 0), then the value part of
+    // its page, masked at the sequence's end (only the sequence's last page
+    // can be partial)
+    const int P = strm * (nit - 1) + st;
+    if (nit > 1) {
+      advance(nit - 1);
+      value_part(part[1], 0, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      if (P < span) key_part(slot_of(nit - 1), part[0]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (nit == 1)
-      last(0, C0{});
-    else if (i & 1)
-      last(i, C1{});
-    else
-      last(i, C0{});
+    if (P < span) value_part(part[0], (p0 + P) * kBlockSize + 4 * c, std::false_type{});
   } else {
     // both parts of a page in its own iteration (fewer registers live)
     auto iteration = [&](int i, auto full_tag) {
