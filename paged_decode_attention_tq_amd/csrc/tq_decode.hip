@@ -388,7 +388,6 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0;
     int32_t* dst = reinterpret_cast<int32_t*>(lds + a.bt_base);
     for (int i = tid; i < span; i += 64 * W) dst[i] = bt[i];
-    if (tid < 16) reinterpret_cast<uint32_t*>(lds + kDecodeLdsBytes - 64)[tid] = 0u;
   }
   __syncthreads();
 
