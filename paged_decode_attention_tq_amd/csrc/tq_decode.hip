@@ -162,9 +162,9 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   using KT = PairTable<KB>;
   using VT = PairTable<VB>;
   constexpr bool kShareV = (KB == VB);
-  // run a page's value part one iteration after its key part (registers allow it
-  // when a value index word per token row slice suffices)
-  constexpr bool kSplit = (VB == 2 || VB == 4) && CONTIG && MAXLD == 3;
+  // run a page's value part one iteration after its key part (registers allow
+  // it with whole-page staging and at most three copies per wave and stage)
+  constexpr bool kSplit = CONTIG && MAXLD == 3;
   // LDS: lookup tables at 0 (so their addresses need no base), then two
   // stage slots, then the split's block ids
   constexpr int kVTab = 0;
