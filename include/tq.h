@@ -135,7 +135,7 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  *   v_pages      same with v_bits.
  *   block_table  device, int32 [batch, max_blocks_per_seq]; entries for pages
  *                beyond a sequence's length are never read.
- *   seq_lens     device, int32 [batch], each in 0..max_seq_len.
+ *   seq_lens     device, int32 [batch], each in 0..max_seq_len (<= 0: zeros).
  *   max_seq_len  host upper bound of seq_lens (sizes the work split).
  *   scale        softmax scale; <= 0 selects 1/sqrt(head_dim).
  *   out          device, fp32 [batch, num_q_heads, head_dim].
@@ -144,8 +144,11 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  * Supported: head_dim 128, block_size 16, k_bits/v_bits 2..5,
  * num_q_heads / num_kv_heads in 1..64 (TQ_ERR_UNSUPPORTED otherwise, or when
  * a sequence is so long that its block ids do not fit the on-chip plan).
- * Asynchronous; block ids and lengths are trusted (an out-of-range block id
- * reads out of bounds). */
+ * Asynchronous.  Device-side values are bounded, never trusted: a block id
+ * outside [0, num_blocks) reads as a page of zero rows (norm 0: score 0,
+ * value 0), and a seq_lens entry above max_blocks_per_seq * block_size (or
+ * above the pages the work split planned for max_seq_len) is clamped to it,
+ * so no memory outside the given buffers is read. */
 tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype,
                           int batch, int num_q_heads, int num_kv_heads,
                           const uint8_t* k_pages, int k_bits,

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   const int s = unit % S;
   const int hg = (unit / S) % a.head_groups;
   const int b = unit / (S * a.head_groups);
-  const int L = __builtin_amdgcn_readfirstlane(a.seq_lens[b]);
+  const int L = __builtin_amdgcn_readfirstlane(min(a.seq_lens[b], a.max_len));
   const int npages = (L + kBlockSize - 1) / kBlockSize;
   const int p0 = s * a.pages_per_split;
   if (p0 >= npages) return;  // the whole workgroup leaves together
@@ -300,13 +300,13 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     for (int d = 0; d < MAXLD; ++d) {
       const int P = si * strm + ld_j[d];
       if (d < n_ld && P < span) {
-        const int blk = __builtin_amdgcn_readfirstlane(bt_lds[P]);
+        const int blk = __builtin_amdgcn_readfirstlane(bt_lds[P]);  // -1: out of range
         const uint64_t pool = ((uint64_t)ld_hi[d] << 32) | ld_lo[d];
-        const uint64_t base = pool + (uint64_t)((int64_t)blk * ld_pb[d]);
+        const uint64_t base = pool + (uint64_t)((int64_t)max(blk, 0) * ld_pb[d]);
         i32x4 rs;
         rs.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
         rs.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu));
-        rs.z = ld_pb[d];
+        rs.z = blk < 0 ? 0 : ld_pb[d];  // a zero-sized buffer reads zeros
         rs.w = 0x00020000;
         const uint32_t dst = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ld_dst[d] + slot * stage_bytes));
         if (ld_ok[d]) copy_chunk_to_lds(rs, dst, ld_voff[d], ld_soff[d]);
@@ -387,7 +387,10 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   {
     const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq + p0;
     int32_t* dst = reinterpret_cast<int32_t*>(lds + a.bt_base);
-    for (int i = tid; i < span; i += 64 * W) dst[i] = bt[i];
+    for (int i = tid; i < span; i += 64 * W) {
+      const int v = bt[i];
+      dst[i] = (v >= 0 && (int64_t)v < a.num_blocks) ? v : -1;
+    }
   }
   __syncthreads();
 
@@ -803,7 +806,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int unit = __builtin_amdgcn_workgroup_id_x() * 4 + (tid >> 6);
   if (unit >= a.batch * a.num_q_heads) return;
   const int b = unit / a.num_q_heads;
-  const int L = a.seq_lens[b];
+  const int L = min(a.seq_lens[b], a.max_len);
   float* o = a.out + (int64_t)unit * kHeadDim;
   if (L <= 0) {
     o[lane] = 0.0f;

@@ -482,6 +482,13 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   d.group = group;
   d.q_groups = p.q_groups;
   d.max_blocks_per_seq = max_blocks_per_seq;
+  d.num_blocks = num_blocks;
+  {
+    // a device-side length beyond the block table or the planned splits is
+    // clamped, so no page past them is ever read
+    const long long cap_pages = std::min<long long>(max_blocks_per_seq, (long long)p.num_splits * p.pages_per_split);
+    d.max_len = (int)std::min<long long>(cap_pages * block_size, 0x7fffffffLL);
+  }
   d.kv_per_wg = p.kv_per_wg;
   d.head_groups = p.head_groups;
   d.streams = p.streams;
@@ -521,6 +528,7 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   m.num_q_heads = num_q_heads;
   m.pages_per_split = p.pages_per_split;
   m.num_splits = p.num_splits;
+  m.max_len = d.max_len;
   m.inv_v_scale_over_sqrt_d = (float)(1.0 / ((double)v_scale * std::sqrt((double)kHeadDim)));
   std::memcpy(m.sign_bits, ctx->sign_bits, sizeof(m.sign_bits));
   return hip_status(tq::launch_merge(m, (hipStream_t)stream));

@@ -1,5 +1,5 @@
 // Internal structures shared by the host code (tq_host.cpp) and the HIP
-// kernels (tq_kernels.hip).  Not part of the public ABI.
+// kernels (tq_write.hip, tq_decode.hip).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,8 +32,8 @@ struct WriteArgs {
 // (sequence, group of kv_per_wg KV heads, split of pages_per_split pages)
 // with waves = kv_per_wg * q_groups * streams waves: each wave owns one KV
 // head, one group of up to 8 of its query heads, and one page of every
-// stage (streams consecutive pages).  The workgroup loads each stage into
-// registers one iteration ahead and stores it into one of two LDS slots.
+// stage (streams consecutive pages).  The workgroup copies each stage
+// straight into one of two LDS slots, one stage ahead of the compute.
 struct DecodeArgs {
   const void* q;                 // [B, Hq, 128]
   const uint8_t* k_pages;
@@ -44,6 +44,8 @@ struct DecodeArgs {
   float* part_lse;               // [B, Hq, S]       log2-sum-exp2 of the split
   int64_t k_page_bytes;
   int64_t v_page_bytes;
+  int64_t num_blocks;            // block ids outside [0, num_blocks) read as zero rows
+  int32_t max_len;               // lengths are clamped to this (the block table and split coverage)
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -86,6 +88,7 @@ struct MergeArgs {
   int32_t num_q_heads;
   int32_t pages_per_split;
   int32_t num_splits;
+  int32_t max_len;               // as DecodeArgs::max_len
   float inv_v_scale_over_sqrt_d; // 1 / (v_scale * sqrt(128))
   uint32_t sign_bits[kHeadDim / 32];
 };

@@ -158,3 +158,42 @@ def test_repeated_calls_are_deterministic(ctx):
     a = _decode(ctx, w, q, kpt, vpt)
     b = _decode(ctx, w, q, kpt, vpt)
     assert np.array_equal(a, b)
+
+
+def test_out_of_range_block_ids_and_lengths(ctx):
+    # Block ids outside [0, num_blocks) read as zero rows, and a device length
+    # beyond the block table is clamped to it.  The page tensors are views into
+    # larger buffers whose extra pages hold 0xFF bytes, and the workspace has
+    # slack, so even an unbounded read would stay inside allocated memory (and
+    # show up as a mismatch, not a fault).
+    w = workloads.make_workload("bounds", num_q_heads=8, num_kv_heads=2, seq_lens=[100, 40], seed=21)
+    print(f"[decode] bounds B={w.batch} lens={w.seq_lens.tolist()} table={w.block_table.shape}", flush=True)
+    codec, _, _, kp, vp = _oracle_pipeline(w)
+    NB = kp.shape[0]
+    max_blocks = w.block_table.shape[1]
+    bt = w.block_table.copy()
+    bt[0, 2] = NB       # one past the end
+    bt[0, 4] = -2       # negative
+    dev_lens = np.array([100, 40 + 10000], dtype=np.int32)
+    # reference: the two bad ids point at appended zero pages; length 1 clamped
+    zero = np.zeros((2,) + kp.shape[1:], dtype=np.uint8)
+    bt_ref = bt.copy()
+    bt_ref[0, 2], bt_ref[0, 4] = NB, NB + 1
+    ref_lens = np.array([100, max_blocks * w.block_size], dtype=np.int32)
+    q = w.queries()
+    ref = oracle.paged_decode(q, np.concatenate([kp, zero]), np.concatenate([vp, zero]), bt_ref, ref_lens,
+                              w.k_bits, w.v_bits, codec.signs, codec.centroids32(w.k_bits),
+                              codec.centroids32(w.v_bits))
+    pages = []
+    for p in (kp, vp):
+        big = torch.full((NB + 3,) + p.shape[1:], 0xFF, dtype=torch.uint8, device="cuda")
+        big[2:2 + NB] = torch.from_numpy(p).cuda()
+        pages.append(big[2:2 + NB])
+    need = api.decode_workspace_bytes(ctx, w.batch, w.num_q_heads, w.num_kv_heads, max_blocks * w.block_size)
+    ws = torch.zeros(need + (1 << 16), dtype=torch.uint8, device="cuda")
+    out = api.paged_decode(ctx, torch.from_numpy(q).cuda(), pages[0], pages[1], torch.from_numpy(bt).cuda(),
+                           torch.from_numpy(dev_lens).cuda(), w.k_bits, w.v_bits,
+                           max_seq_len=max_blocks * w.block_size, workspace=ws)
+    torch.cuda.synchronize()
+    r = compare_decode(out.cpu().numpy(), ref, "bounded block ids and lengths")
+    print(f"  max|d| relL2 {r}", flush=True)
