@@ -174,9 +174,13 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   const int S = a.num_splits;
   const int unit = __builtin_amdgcn_workgroup_id_x();
   const int tid = __builtin_amdgcn_workitem_id_x();
-  const int s = unit % S;
-  const int hg = (unit / S) % a.head_groups;
-  const int b = unit / (S * a.head_groups);
+  // split-major order: every sequence's first split is dispatched before any
+  // second split, so in a ragged batch the short tails of long sequences come
+  // last and the CUs finish close together
+  const int bh = unit % (a.batch * a.head_groups);
+  const int s = unit / (a.batch * a.head_groups);
+  const int hg = bh % a.head_groups;
+  const int b = bh / a.head_groups;
   const int L = __builtin_amdgcn_readfirstlane(min(a.seq_lens[b], a.max_len));
   const int npages = (L + kBlockSize - 1) / kBlockSize;
   const int p0 = s * a.pages_per_split;
