@@ -228,7 +228,8 @@ int device_cu_count() {
 // over each token's slice; two stage slots, the lookup tables and the block
 // ids share the CU's LDS, which bounds kv_per_wg and streams.  The split
 // count aims at one workgroup per CU (a workgroup fills a CU's LDS), keeps at
-// least 8 splits for the longest sequence (so ragged batches balance) and at
+// least 4 splits for the longest sequence (so ragged batches balance; more,
+// smaller splits cost more in per-workgroup set-up than they gain) and at
 // most 64 (the merge holds one split weight per lane).
 struct SplitPlan {
   int q_groups;
@@ -259,7 +260,7 @@ bool plan_split(int batch, int num_kv_heads, int group, int max_seq_len, int k_b
   const int rb[2] = {(int)tq_row_bytes(kHeadDim, k_bits), (int)tq_row_bytes(kHeadDim, v_bits)};
   const int tables = tq::decode_table_bytes(k_bits, v_bits);
   const int max_pages = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
-  const int bt_cap = std::max(1, std::min((max_pages + 7) / 8, std::max(2048, (max_pages + 63) / 64)));
+  const int bt_cap = std::max(1, std::min((max_pages + 3) / 4, std::max(2048, (max_pages + 63) / 64)));
   const int bt_bytes = 4 * bt_cap;
   bool found = false;
   for (int kv = num_kv_heads; kv >= 1 && !found; --kv) {
@@ -304,7 +305,7 @@ bool plan_split(int batch, int num_kv_heads, int group, int max_seq_len, int k_b
   long long s0 = (target + units - 1) / units;
   if (s0 < 1) s0 = 1;
   long long pps = (max_pages + s0 - 1) / s0;
-  const long long cap = (max_pages + 7) / 8;
+  const long long cap = (max_pages + 3) / 4;
   if (pps > cap) pps = cap;
   if (pps > bt_cap) pps = bt_cap;
   const long long floor_pps = (max_pages + 63) / 64;
