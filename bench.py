@@ -114,8 +114,8 @@ def traffic_bytes():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="long_context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -230,6 +230,7 @@ def main():
         },
         "packed_kv_bytes": packed,
         "decode_ms": float(dec_ms.mean()),
+        "decode_ms_median": float(np.median(dec_ms)),
         "decode_ms_min": float(dec_ms.min()),
         "packed_kv_gbps": achieved,
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
