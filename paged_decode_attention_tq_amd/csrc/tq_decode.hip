@@ -21,16 +21,21 @@
 //          weights w = p * n_v stay below 2^9 and fit fp16; the reference is
 //          raised lazily, only when the page maximum exceeds it by 8.
 //  values  acc[dim][h] += sum_t V^[t][dim] w[t][h] with
-//          v_mfma_f32_16x16x16_f16: A = dequantised values (16 dims x 16
-//          tokens), B = weights, again [w_hi | w_lo] in the columns for G <= 8.
+//          v_mfma_f32_16x16x32_f16: A = dequantised value pairs (16 dim
+//          pairs x (16 tokens x 2 parities)), B = the weights w_hi, then in a
+//          second MFMA w_lo, each placed in the column half of its dim parity
+//          (columns h: even dims, h + 8: odd dims).
 // Lane layout (l = lane, n = l & 15, c = l >> 4):
-//  K loads  token n, dims 32c..32c+31 (4*KB contiguous bytes of its row);
-//  V loads  tokens 4c..4c+3, dims 8n..8n+7 (VB bytes of each row);
+//  K reads  token n, dims 32c..32c+31 (4*KB contiguous bytes of its row);
+//  V reads  tokens 4c..4c+3, dims 8n..8n+7 (VB bits per dim of each row);
 //  scores   tokens 4c+r (r = 0..3), column n;
-//  acc      column n, dims 32c + 8r + blk (blk = 0..7).
+//  acc      column n, dims 32c + 8r + 2 blk + (n >> 3) (blk = 0..3).
 // Dequantisation reads LDS pair tables: row p = i0 | i1 << b holds the fp16
-// pair (c[i0], c[i1]) replicated once per lane of a half-wave (bank-conflict
-// free), hi part then lo part.
+// pair (c[i0], c[i1]) and the fp16 pair of its rounding residuals (8 bytes),
+// replicated once per lane of a half-wave (bank-conflict free); keys read
+// both halves, values only the pair (the upper half of the replicas stores
+// the two dwords swapped, so that a half-wave's value reads also hit
+// distinct banks).
 
 #include "tq_internal.h"
 #include "tq_device.h"
@@ -454,10 +459,8 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   // Key part: the key indices and table lookups (LDS), the score MFMAs, and
   // the page's value index words and norms, all left in registers.  Value
   // part: value table lookups, softmax, value MFMAs.  The stage loop runs a
-  // page's value part one iteration after its key part, which frees the
-  // page's stage slot a whole iteration early; half the waves of each SIMD
-  // run the two parts in the opposite order, so that the LDS-heavy key part
-  // of some waves overlaps the ALU-heavy value part of others.
+  // page's value part one iteration after its key part (when registers allow
+  // it), which frees the page's stage slot a whole iteration early.
   constexpr int kVW = (VB == 3 || VB == 5) ? 2 : 1;  // value index words per token row slice
   struct PagePart {
     floatx4 sc;          // raw scores (fp16 hi and lo columns not yet summed)
