@@ -74,7 +74,7 @@ def test_bits_combinations(ctx, kb, vb):
     _run(ctx, w)
 
 
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16, 64])
 def test_group_sizes(ctx, G):
     w = workloads.make_workload(f"group{G}", num_q_heads=2 * G, num_kv_heads=2, seq_lens=[200, 45, 16],
                                 seed=G, outlier_frac=0.02)
@@ -197,3 +197,10 @@ def test_out_of_range_block_ids_and_lengths(ctx):
     torch.cuda.synchronize()
     r = compare_decode(out.cpu().numpy(), ref, "bounded block ids and lengths")
     print(f"  max|d| relL2 {r}", flush=True)
+
+
+def test_long_sequence_max_splits(ctx):
+    # one 65547-token sequence (4097 pages): the plan's maximum of 64 splits,
+    # 65 pages each and 2 in the last, with a ragged last page
+    w = workloads.make_workload("long1", num_q_heads=8, num_kv_heads=1, seq_lens=[65536 + 11], seed=23)
+    _run(ctx, w)
