@@ -2,7 +2,7 @@
 
 A step is one decode step of the whole hot path for a batch of sequences:
 write the new token's K row and V row of every sequence into the pages
-(tq_write_kv, the row writer), then run the single-query paged decode over
+(the row writer, K and V in one launch: tq_write_kv_pair), then run the single-query paged decode over
 each sequence's full context (tq_paged_decode).  The workload defaults to
 the long-context configuration: 8 sequences x 131072 tokens, K4/V4, 64 query
 heads over 8 KV heads, head_dim 128, 16-token pages in a random permutation
@@ -180,8 +180,7 @@ def main():
             flush_rd.sum()
         if i is not None:
             ev[i][0].record()
-        api.write_kv(ctx, k_new, kp, new_slots, w.k_bits, err_count=err, check_slots=False)
-        api.write_kv(ctx, v_new, vp, new_slots, w.v_bits, err_count=err, check_slots=False)
+        api.write_kv_pair(ctx, k_new, v_new, kp, vp, new_slots, w.k_bits, w.v_bits, err_count=err, check_slots=False)
         if i is not None:
             ev[i][1].record()
         api.paged_decode(ctx, q_d, kp, vp, bt, lens, w.k_bits, w.v_bits, max_seq_len=w.max_seq_len,

@@ -122,6 +122,19 @@ tq_status tq_write_kv(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype,
                       int64_t num_blocks, int block_size, const int64_t* slots,
                       int bits, int32_t* err_count, void* stream);
 
+/* K and V rows of the same tokens in one launch (the same write as
+ * tq_write_kv for K, then for V, with the same slots; "vLLM Usage", "Slot
+ * Mapping" and "TQ Packed Page Contract").  raw_k / raw_v, k_pages / v_pages
+ * and bits as in tq_write_kv per component; both page tensors have
+ * num_blocks pages of block_size tokens.  An out-of-range slot is skipped by
+ * both components and counted once in *err_count.  Asynchronous, allocates
+ * nothing. */
+tq_status tq_write_kv_pair(const tq_ctx* ctx, const void* raw_k, const void* raw_v,
+                           tq_dtype raw_dtype, int64_t num_tokens, int num_kv_heads,
+                           uint8_t* k_pages, int k_bits, uint8_t* v_pages, int v_bits,
+                           int64_t num_blocks, int block_size, const int64_t* slots,
+                           int32_t* err_count, void* stream);
+
 /* Bytes of device workspace tq_paged_decode needs for these sizes. */
 size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
                                  int num_kv_heads, int max_seq_len, int block_size);

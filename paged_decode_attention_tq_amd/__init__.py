@@ -13,4 +13,5 @@ from .api import (  # noqa: F401
     rht_signs,
     row_bytes,
     write_kv,
+    write_kv_pair,
 )

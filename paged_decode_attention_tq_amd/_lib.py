@@ -39,6 +39,11 @@ SIGNATURES = {
         [_c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int64,
          _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p],
     ),
+    "tq_write_kv_pair": (
+        _c.c_int,
+        [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int,
+         _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p],
+    ),
     "tq_decode_workspace_bytes": (
         _c.c_size_t, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
     "tq_paged_decode": (

@@ -21,6 +21,7 @@ __all__ = [
     "rht_signs",
     "Context",
     "write_kv",
+    "write_kv_pair",
     "decode_workspace_bytes",
     "paged_decode",
 ]
@@ -108,6 +109,40 @@ def write_kv(ctx: Context, raw: torch.Tensor, pages: torch.Tensor, slots: torch.
         n_bad = int(err_count.item())
         if n_bad:
             raise TQError(f"tq_write_kv: {n_bad} slot(s) outside the allocated pages")
+        return n_bad
+    return 0
+
+
+def write_kv_pair(ctx: Context, raw_k: torch.Tensor, raw_v: torch.Tensor, k_pages: torch.Tensor,
+                  v_pages: torch.Tensor, slots: torch.Tensor, k_bits: int, v_bits: int,
+                  err_count: torch.Tensor | None = None, check_slots: bool = True) -> int:
+    """``write_kv`` for K and for V of the same tokens, in one launch."""
+    _need(raw_k.is_cuda and raw_v.is_cuda and k_pages.is_cuda and v_pages.is_cuda and slots.is_cuda,
+          "tensors must be on the GPU")
+    _need(raw_k.shape == raw_v.shape and raw_k.dtype == raw_v.dtype, "raw_k / raw_v shape or dtype mismatch")
+    _need(raw_k.dim() == 3 and raw_k.shape[2] == ctx.head_dim and raw_k.is_contiguous() and raw_v.is_contiguous(),
+          "raw must be [N, Hkv, d]")
+    for name, pg, bits in (("k_pages", k_pages, k_bits), ("v_pages", v_pages, v_bits)):
+        _need(pg.dtype == torch.uint8 and pg.dim() == 4 and pg.is_contiguous(), f"{name} must be uint8 4-D")
+        _need(pg.shape[3] == row_bytes(ctx.head_dim, bits), f"{name} row_bytes does not match bits")
+    NB, BS, Hkv, _ = k_pages.shape
+    _need(tuple(v_pages.shape[:3]) == (NB, BS, Hkv), "k_pages / v_pages geometry mismatch")
+    _need(raw_k.shape[1] == Hkv, "num_kv_heads mismatch")
+    _need(slots.dtype == torch.int64 and slots.shape == (raw_k.shape[0],) and slots.is_contiguous(),
+          "slots must be int64 [N]")
+    _need(raw_k.dtype in _DTYPES, "raw dtype must be fp32/fp16/bf16")
+    own = err_count is None and check_slots
+    if own:
+        err_count = torch.zeros(1, dtype=torch.int32, device=raw_k.device)
+    st = _lib.lib().tq_write_kv_pair(
+        ctx.handle, raw_k.data_ptr(), raw_v.data_ptr(), _DTYPES[raw_k.dtype], raw_k.shape[0], Hkv,
+        k_pages.data_ptr(), k_bits, v_pages.data_ptr(), v_bits, NB, BS, slots.data_ptr(),
+        err_count.data_ptr() if err_count is not None else None, _stream(raw_k))
+    check(st, "tq_write_kv_pair")
+    if check_slots:
+        n_bad = int(err_count.item())
+        if n_bad:
+            raise TQError(f"tq_write_kv_pair: {n_bad} slot(s) outside the allocated pages")
         return n_bad
     return 0
 

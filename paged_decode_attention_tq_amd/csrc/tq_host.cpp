@@ -381,20 +381,25 @@ tq_status tq_ctx_destroy(tq_ctx* ctx) {
   return TQ_OK;
 }
 
-tq_status tq_write_kv(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype, int64_t num_tokens,
-                      int num_kv_heads, uint8_t* pages, int64_t num_blocks, int block_size,
-                      const int64_t* slots, int bits, int32_t* err_count, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validate one component's write and fill its kernel arguments.
+tq_status make_write_args(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype, int64_t num_tokens,
+                          int num_kv_heads, uint8_t* pages, int64_t num_blocks, int block_size,
+                          const int64_t* slots, int bits, int32_t* err_count, tq::WriteArgs* out) {
   if (!ctx || num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || block_size <= 0)
     return TQ_ERR_INVALID_ARG;
   if (raw_dtype != TQ_F32 && raw_dtype != TQ_F16 && raw_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
   if (!bits_ok(bits)) return TQ_ERR_UNSUPPORTED;
-  if (num_tokens == 0) return TQ_OK;
+  tq::WriteArgs& a = *out;
+  std::memset(&a, 0, sizeof(a));
+  if (num_tokens == 0) return TQ_OK;  // nothing to write (pointers unused)
   if (!raw || !pages || !slots) return TQ_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(raw) & 3) || (reinterpret_cast<uintptr_t>(pages) & 3) ||
       (reinterpret_cast<uintptr_t>(slots) & 7))
     return TQ_ERR_ALIGNMENT;
-  tq::WriteArgs a;
-  std::memset(&a, 0, sizeof(a));
   a.raw = raw;
   a.pages = pages;
   a.slots = slots;
@@ -408,7 +413,36 @@ tq_status tq_write_kv(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype, in
   std::memcpy(a.sign_bits, ctx->sign_bits, sizeof(a.sign_bits));
   const int n = 1 << bits;
   for (int j = 0; j < n / 2 - 1; ++j) a.pos_bounds[j] = ctx->bound[bits][n / 2 + j];
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_write_kv(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype, int64_t num_tokens,
+                      int num_kv_heads, uint8_t* pages, int64_t num_blocks, int block_size,
+                      const int64_t* slots, int bits, int32_t* err_count, void* stream) {
+  tq::WriteArgs a;
+  const tq_status st = make_write_args(ctx, raw, raw_dtype, num_tokens, num_kv_heads, pages, num_blocks,
+                                       block_size, slots, bits, err_count, &a);
+  if (st != TQ_OK || num_tokens == 0) return st;
   return hip_status(tq::launch_write(a, (int)raw_dtype, bits, (hipStream_t)stream));
+}
+
+tq_status tq_write_kv_pair(const tq_ctx* ctx, const void* raw_k, const void* raw_v, tq_dtype raw_dtype,
+                           int64_t num_tokens, int num_kv_heads, uint8_t* k_pages, int k_bits,
+                           uint8_t* v_pages, int v_bits, int64_t num_blocks, int block_size,
+                           const int64_t* slots, int32_t* err_count, void* stream) {
+  tq::WriteArgs k, v;
+  tq_status st = make_write_args(ctx, raw_k, raw_dtype, num_tokens, num_kv_heads, k_pages, num_blocks,
+                                 block_size, slots, k_bits, err_count, &k);
+  if (st != TQ_OK) return st;
+  // an out-of-range slot is counted once (by the K rows); both components skip it
+  st = make_write_args(ctx, raw_v, raw_dtype, num_tokens, num_kv_heads, v_pages, num_blocks, block_size,
+                       slots, v_bits, nullptr, &v);
+  if (st != TQ_OK || num_tokens == 0) return st;
+  return hip_status(tq::launch_write_pair(k, v, (int)raw_dtype, k_bits, v_bits, (hipStream_t)stream));
 }
 
 size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads, int num_kv_heads,

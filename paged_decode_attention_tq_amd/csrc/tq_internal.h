@@ -94,6 +94,9 @@ struct MergeArgs {
 };
 
 hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t stream);
+// K and V rows of the same tokens (same num_rows) in one launch
+hipError_t launch_write_pair(const WriteArgs& k, const WriteArgs& v, int raw_dtype, int k_bits, int v_bits,
+                             hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, hipStream_t stream);
 int decode_table_bytes(int k_bits, int v_bits);  // LDS bytes of the decode lookup tables
 int decode_merge_lds_bytes();                     // LDS bytes of the stream merge

@@ -55,12 +55,13 @@ __device__ __forceinline__ void load_row32(const void* raw, int64_t elem_off, fl
   }
 }
 
+// The rows of workgroup `wg` (64 rows, one per 4-lane quad) of one call.
 template <int BITS, int DT>
-__global__ __launch_bounds__(256) void write_rows_kernel(WriteArgs a) {
+__device__ __forceinline__ void write_rows(const WriteArgs& a, int64_t wg) {
   constexpr int N = 1 << BITS;
   constexpr int HALF = N / 2;
   const int q = threadIdx.x & 3;
-  const int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int64_t row = wg * 64 + (threadIdx.x >> 2);
   if (row >= a.num_rows) return;  // uniform per quad
   const int64_t tok = row / a.num_kv_heads;
   const int head = (int)(row - tok * a.num_kv_heads);
@@ -163,6 +164,22 @@ __global__ __launch_bounds__(256) void write_rows_kernel(WriteArgs a) {
   if (q == 3) *reinterpret_cast<float*>(dst + a.row_bytes - 4) = n32;
 }
 
+template <int BITS, int DT>
+__global__ __launch_bounds__(256) void write_rows_kernel(WriteArgs a) {
+  write_rows<BITS, DT>(a, blockIdx.x);
+}
+
+// K and V rows of the same tokens in one launch: workgroups [0, k_groups)
+// take the K rows, the others the V rows.
+template <int KB, int VB, int DT>
+__global__ __launch_bounds__(256) void write_pair_kernel(WriteArgs k, WriteArgs v, int64_t k_groups) {
+  const int64_t wg = blockIdx.x;
+  if (wg < k_groups)
+    write_rows<KB, DT>(k, wg);
+  else
+    write_rows<VB, DT>(v, wg - k_groups);
+}
+
 template <int BITS>
 static hipError_t launch_write_bits(const WriteArgs& a, int dt, hipStream_t st) {
   const dim3 grid((unsigned)((a.num_rows + 63) / 64)), block(256);
@@ -182,6 +199,42 @@ hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t
     case 3: return launch_write_bits<3>(a, raw_dtype, stream);
     case 4: return launch_write_bits<4>(a, raw_dtype, stream);
     case 5: return launch_write_bits<5>(a, raw_dtype, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int KB, int VB>
+static hipError_t launch_pair_kv(const WriteArgs& k, const WriteArgs& v, int dt, hipStream_t st) {
+  const int64_t groups = (k.num_rows + 63) / 64;
+  const dim3 grid((unsigned)(2 * groups)), block(256);
+  if (dt == 0)
+    hipLaunchKernelGGL((write_pair_kernel<KB, VB, 0>), grid, block, 0, st, k, v, groups);
+  else if (dt == 1)
+    hipLaunchKernelGGL((write_pair_kernel<KB, VB, 1>), grid, block, 0, st, k, v, groups);
+  else
+    hipLaunchKernelGGL((write_pair_kernel<KB, VB, 2>), grid, block, 0, st, k, v, groups);
+  return hipGetLastError();
+}
+
+template <int KB>
+static hipError_t launch_pair_k(const WriteArgs& k, const WriteArgs& v, int dt, int vb, hipStream_t st) {
+  switch (vb) {
+    case 2: return launch_pair_kv<KB, 2>(k, v, dt, st);
+    case 3: return launch_pair_kv<KB, 3>(k, v, dt, st);
+    case 4: return launch_pair_kv<KB, 4>(k, v, dt, st);
+    case 5: return launch_pair_kv<KB, 5>(k, v, dt, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_write_pair(const WriteArgs& k, const WriteArgs& v, int raw_dtype, int k_bits, int v_bits,
+                             hipStream_t stream) {
+  if (k.num_rows == 0) return hipSuccess;
+  switch (k_bits) {
+    case 2: return launch_pair_k<2>(k, v, raw_dtype, v_bits, stream);
+    case 3: return launch_pair_k<3>(k, v, raw_dtype, v_bits, stream);
+    case 4: return launch_pair_k<4>(k, v, raw_dtype, v_bits, stream);
+    case 5: return launch_pair_k<5>(k, v, raw_dtype, v_bits, stream);
   }
   return hipErrorInvalidValue;
 }

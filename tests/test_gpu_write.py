@@ -117,3 +117,39 @@ def test_tiny_preset_pages(ctx, codec):
     w = workloads.preset("tiny")
     for comp in ("k", "v"):
         _check(ctx, codec, w.rows(comp), w.zero_pages(4), w.slots, 4)
+
+
+@pytest.mark.parametrize("kb,vb,dtype", [(4, 4, torch.float16), (4, 2, torch.float16), (3, 5, torch.float32),
+                                         (2, 3, torch.bfloat16)])
+def test_write_pair_equals_two_writes_and_oracle(ctx, codec, kb, vb, dtype):
+    # one launch for K and V gives the bytes of two single-component writes,
+    # which match the oracle; a bad slot is skipped by both and counted once
+    w = workloads.make_workload("pair", k_bits=kb, v_bits=vb, num_q_heads=8, num_kv_heads=4,
+                                seq_lens=[37, 16, 5], seed=31 + kb + vb, drop_frac=0.1, extra_blocks=2)
+    print(f"[write pair] K{kb}V{vb} {dtype} rows={w.num_tokens}x{w.num_kv_heads}", flush=True)
+    kraw = torch.from_numpy(w.rows("k")).to(dtype)
+    vraw = torch.from_numpy(w.rows("v")).to(dtype)
+    slots = w.slots.copy()
+    NB, BS = w.page_shape(kb)[:2]
+    slots[3] = NB * BS + 1  # out of range
+    slots_t = torch.from_numpy(slots).cuda()
+    k0 = np.random.default_rng(kb).integers(0, 256, size=w.page_shape(kb), dtype=np.uint8)
+    v0 = np.random.default_rng(vb + 9).integers(0, 256, size=w.page_shape(vb), dtype=np.uint8)
+    kp, vp = torch.from_numpy(k0).cuda(), torch.from_numpy(v0).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.write_kv_pair(ctx, kraw.cuda(), vraw.cuda(), kp, vp, slots_t, kb, vb, err_count=err, check_slots=False)
+    kp1, vp1 = torch.from_numpy(k0).cuda(), torch.from_numpy(v0).cuda()
+    api.write_kv(ctx, kraw.cuda(), kp1, slots_t, kb, check_slots=False)
+    api.write_kv(ctx, vraw.cuda(), vp1, slots_t, vb, check_slots=False)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    assert np.array_equal(kp.cpu().numpy(), kp1.cpu().numpy())
+    assert np.array_equal(vp.cpu().numpy(), vp1.cpu().numpy())
+    ok = slots.copy()
+    ok[3] = -1
+    written = int((ok >= 0).sum()) * w.num_kv_heads
+    for raw, pages0, got, bits in ((kraw, k0, kp, kb), (vraw, v0, vp, vb)):
+        ref, near = codec.write_kv(raw.float().numpy(), pages0, ok, bits)
+        compare_pages(got.cpu().numpy(), ref, near, bits, written)
+    with pytest.raises(api.TQError):
+        api.write_kv_pair(ctx, kraw.cuda(), vraw.cuda(), kp, vp, slots_t, kb, vb)
