@@ -60,6 +60,15 @@ def test_status_strings_and_argument_errors():
     assert lib.tq_write_kv(h, None, 1, 4, 2, None, 4, 16, None, 4, None, None) == 1  # null raw
     assert lib.tq_write_kv(h, None, 9, 4, 2, None, 4, 16, None, 4, None, None) == 1  # bad dtype
     assert lib.tq_write_kv(h, None, 1, 0, 2, None, 4, 16, None, 4, None, None) == 0  # nothing to do
+    # the K+V pair: each component's arguments are checked the same way
+    pw = lib.tq_write_kv_pair
+    a64 = ctypes.c_void_p(64)  # aligned, never dereferenced: validation fails first
+    assert pw(h, a64, a64, 1, 4, 2, a64, 4, a64, 7, 4, 16, a64, None, None) == 2  # V bits 7
+    assert pw(h, None, None, 1, 4, 2, None, 9, None, 4, 4, 16, None, None, None) == 2  # K bits 9
+    assert pw(h, None, None, 1, 4, 2, None, 4, None, 4, 4, 16, None, None, None) == 1  # null pointers
+    assert pw(h, None, None, 1, 0, 2, None, 4, None, 2, 4, 16, None, None, None) == 0  # nothing to do
+    assert pw(h, ctypes.c_void_p(64), ctypes.c_void_p(66), 1, 4, 2, ctypes.c_void_p(64), 4,
+              ctypes.c_void_p(64), 4, 4, 16, ctypes.c_void_p(64), None, None) == 3  # raw_v misaligned
     p = ctypes.c_void_p(16)
     args = dict(batch=2, hq=128, hkv=1)  # group 128 > 64
     assert lib.tq_paged_decode(h, p, 1, 2, 128, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 2
