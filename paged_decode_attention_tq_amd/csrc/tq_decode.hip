@@ -834,18 +834,20 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
   float y0 = 0.0f, y1 = 0.0f;
   int sidx = 0;
-  for (; sidx + 4 <= ns; sidx += 4) {
-    float v0[4], v1[4], w4[4];
+  // 16 splits per round: all their loads are in flight together
+  constexpr int kU = 16;
+  for (; sidx + kU <= ns; sidx += kU) {
+    float v0[kU], v1[kU], wu[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kU; ++u) {
       v0[u] = pa[(int64_t)(sidx + u) * kHeadDim + lane];
       v1[u] = pa[(int64_t)(sidx + u) * kHeadDim + lane + 64];
-      w4[u] = __shfl(wgt, sidx + u);
+      wu[u] = __shfl(wgt, sidx + u);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      y0 += w4[u] * v0[u];
-      y1 += w4[u] * v1[u];
+    for (int u = 0; u < kU; ++u) {
+      y0 += wu[u] * v0[u];
+      y1 += wu[u] * v1[u];
     }
   }
   for (; sidx < ns; ++sidx) {
