@@ -305,11 +305,18 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   // wave has waited for its vector memory counter and the workgroup has met
   // at a barrier
   auto issue_dma = [&](int si, int slot) {
+    // the block ids first: their LDS reads are in flight together, and one
+    // wait covers them all (read per copy, each would wait on its own)
+    int blk_ids[MAXLD];
+#pragma unroll
+    for (int d = 0; d < MAXLD; ++d) blk_ids[d] = bt_lds[min(si * strm + ld_j[d], span - 1)];
+#pragma unroll
+    for (int d = 0; d < MAXLD; ++d) blk_ids[d] = __builtin_amdgcn_readfirstlane(blk_ids[d]);
 #pragma unroll
     for (int d = 0; d < MAXLD; ++d) {
       const int P = si * strm + ld_j[d];
       if (d < n_ld && P < span) {
-        const int blk = __builtin_amdgcn_readfirstlane(bt_lds[P]);  // -1: out of range
+        const int blk = blk_ids[d];  // -1: out of range
         const uint64_t pool = ((uint64_t)ld_hi[d] << 32) | ld_lo[d];
         const uint64_t base = pool + (uint64_t)((int64_t)max(blk, 0) * ld_pb[d]);
         i32x4 rs;
