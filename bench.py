@@ -133,9 +133,10 @@ def main():
 
     dev = torch.device("cuda:0")
     w = workloads.preset(args.config)
+    kernel = api.decode_kernel(w.batch, w.num_q_heads, w.num_kv_heads, w.max_seq_len, w.k_bits, w.v_bits)
     B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
     log(f"[bench] {w.name}: B={B} L={w.max_seq_len} Hq={Hq} Hkv={Hkv} K{w.k_bits}V{w.v_bits} "
-        f"packed={w.packed_kv_bytes() / 1e9:.3f} GB")
+        f"packed={w.packed_kv_bytes() / 1e9:.3f} GB, {kernel} decode kernel")
 
     t0 = time.perf_counter()
     kraw, vraw, q = w.rows("k", threads=16), w.rows("v", threads=16), w.queries()
@@ -218,7 +219,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 MFMA operands (hi+lo split), fp32 accumulation; u8 packed K4/V4",
+        "dtype": (f"u8 packed K{w.k_bits}/V{w.v_bits} pages; keys, queries and softmax weights as fp16 hi+lo MFMA "
+                  "operands, value centroids fp16 (hi only, pre-scaled), fp32 accumulation"),
         "data": "synthetic (seeded N(0,1) fp16 K/V/q, random page permutation)",
         "config": {
             "workload": f"{w.name}: batch {B} x {w.max_seq_len} tokens, Hq {Hq}, Hkv {Hkv}, head_dim {d}, "
@@ -236,7 +238,7 @@ def main():
         "context_tokens_per_s": float(w.num_tokens) / dec_s,
         "roofline": {
             "bound": "hbm",
-            "kernel": "tq_paged_decode (split + merge kernels)",
+            "kernel": f"tq_paged_decode, {kernel} decode kernel + merge kernel",
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -102,7 +102,9 @@ tq_status tq_ctx_create(int head_dim, uint64_t rht_seed, tq_ctx** out);
 tq_status tq_ctx_destroy(tq_ctx* ctx);
 
 /* Write rows into pages ("vLLM Usage", "Slot Mapping" and "TQ Packed Page
- * Contract", write_tq4_kv).
+ * Contract", write_tq4_kv).  Arguments are validated first (no device needed);
+ * TQ_ERR_NO_DEVICE when the current device is not a gfx950 (checked once per
+ * device).
  *   raw       device, [num_tokens, num_kv_heads, head_dim] of raw_dtype,
  *             contiguous, 4-byte aligned (16-byte aligned for best speed).
  *   pages     device, uint8 [num_blocks, block_size, num_kv_heads,
@@ -135,9 +137,25 @@ tq_status tq_write_kv_pair(const tq_ctx* ctx, const void* raw_k, const void* raw
                            int64_t num_blocks, int block_size, const int64_t* slots,
                            int32_t* err_count, void* stream);
 
-/* Bytes of device workspace tq_paged_decode needs for these sizes. */
+/* Bytes of device workspace tq_paged_decode needs for these sizes (the
+ * split partials: a normalised rotated sum and a log-sum-exp per query head
+ * and split).  The count of splits follows the current device's compute
+ * units, so the value holds for the device current at this call; a workspace
+ * sized on a device with fewer compute units can be too small on another, and
+ * tq_paged_decode then returns TQ_ERR_WORKSPACE without launching anything.
+ * ctx and block_size are not used (the size covers every bit width).
+ * Returns 0 for a non-positive batch or head count or a negative length. */
 size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
                                  int num_kv_heads, int max_seq_len, int block_size);
+
+/* Which decode kernel tq_paged_decode runs for these sizes on the current
+ * device: "wave" (every wave owns all KV heads and walks its own pages;
+ * 1, 2 or 4 KV heads with at most 8 query heads each), "staged" (a
+ * workgroup stages whole pages for all its waves), or NULL when the sizes are
+ * not supported.  The environment variable TQ_DECODE_KERNEL=staged|wave
+ * overrides the choice where the sizes allow it.  Host-only; static string. */
+const char* tq_decode_kernel(int batch, int num_q_heads, int num_kv_heads,
+                             int max_seq_len, int k_bits, int v_bits);
 
 /* Single-query paged decode attention over TQ pages ("Architecture",
  * "Diagnostic vs Serving Paths": the paged decode reads packed pages and
@@ -157,7 +175,9 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
  * Supported: head_dim 128, block_size 16, k_bits/v_bits 2..5,
  * num_q_heads / num_kv_heads in 1..64 (TQ_ERR_UNSUPPORTED otherwise, or when
  * a sequence is so long that its block ids do not fit the on-chip plan).
- * Asynchronous.  Device-side values are bounded, never trusted: a block id
+ * Asynchronous.  TQ_ERR_NO_DEVICE when the current device is not a gfx950
+ * (checked after the arguments and the workspace size).  Device-side values
+ * are bounded, never trusted: a block id
  * outside [0, num_blocks) reads as a page of zero rows (norm 0: score 0,
  * value 0), and a seq_lens entry above max_blocks_per_seq * block_size (or
  * above the pages the work split planned for max_seq_len) is clamped to it,

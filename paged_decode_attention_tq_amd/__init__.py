@@ -8,6 +8,7 @@ from .api import (  # noqa: F401
     TQError,
     Context,
     codebook,
+    decode_kernel,
     decode_workspace_bytes,
     paged_decode,
     rht_signs,

@@ -23,6 +23,7 @@ __all__ = [
     "write_kv",
     "write_kv_pair",
     "decode_workspace_bytes",
+    "decode_kernel",
     "paged_decode",
 ]
 
@@ -152,6 +153,12 @@ def decode_workspace_bytes(ctx: Context, batch, num_q_heads, num_kv_heads, max_s
                                                     max_seq_len, block_size))
 
 
+def decode_kernel(batch, num_q_heads, num_kv_heads, max_seq_len, k_bits, v_bits) -> str | None:
+    """'wave' or 'staged': the decode kernel these sizes run on the current device (None: unsupported)."""
+    name = _lib.lib().tq_decode_kernel(batch, num_q_heads, num_kv_heads, max_seq_len, k_bits, v_bits)
+    return name.decode() if name else None
+
+
 def paged_decode(ctx: Context, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
                  block_table: torch.Tensor, seq_lens: torch.Tensor, k_bits: int, v_bits: int,
                  max_seq_len: int | None = None, scale: float | None = None,
@@ -186,3 +193,4 @@ def paged_decode(ctx: Context, q: torch.Tensor, k_pages: torch.Tensor, v_pages: 
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
     check(st, "tq_paged_decode")
     return out
+

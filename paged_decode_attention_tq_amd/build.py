@@ -3,8 +3,9 @@
     python -m paged_decode_attention_tq_amd.build
 
 Compiles ``csrc/tq_host.cpp`` (host C++: the C ABI, context, codebook
-solver), ``csrc/tq_write.hip`` (row writer) and ``csrc/tq_decode.hip``
-(paged decode and merge) for gfx950 with hipcc into
+solver), ``csrc/tq_write.hip`` (row writer), ``csrc/tq_decode.hip`` (staged
+paged decode and merge) and ``csrc/tq_decode_wave.hip`` (wave-private paged
+decode and merge) for gfx950 with hipcc into
 ``paged_decode_attention_tq_amd/libtq.so``.
 """
 
@@ -33,7 +34,12 @@ HIP_FLAGS = [
 
 # per-source extras: the decode never produces NaNs on valid input, so it
 # drops IEEE NaN quieting (fmaxf then needs no canonicalisation)
-EXTRA_FLAGS = {"tq_decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+SOURCES = ("tq_host.cpp", "tq_write.hip", "tq_decode.hip", "tq_decode_wave.hip")
+
+EXTRA_FLAGS = {
+    "tq_decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+    "tq_decode_wave.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+}
 
 
 def hipcc():
@@ -44,23 +50,35 @@ def hipcc():
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the library (always) and return its path."""
-    objs = []
+    """Compile the library (always) and return its path.  The sources compile
+    in parallel; the link waits for all of them."""
     tmp = LIB + ".tmp"
-    cmds = []
-    for src in ("tq_host.cpp", "tq_write.hip", "tq_decode.hip"):
+    objs, compiles = [], []
+    for src in SOURCES:
         obj = os.path.join(CSRC, src + ".o")
-        cmds.append([hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
-                     os.path.join(CSRC, src), "-o", obj])
+        compiles.append([hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+                         os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
-    cmds.append([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
-    for cmd in cmds:
+    procs = []
+    for cmd in compiles:
         if verbose:
             print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            sys.stderr.write(res.stdout + res.stderr)
-            raise RuntimeError(f"build failed: {' '.join(cmd)}")
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = None
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0 and failed is None:
+            sys.stderr.write(out)
+            failed = cmd
+    if failed:
+        raise RuntimeError(f"build failed: {' '.join(failed)}")
+    link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"build failed: {' '.join(link)}")
     os.replace(tmp, LIB)
     for obj in objs:
         os.remove(obj)

@@ -317,6 +317,72 @@ bool plan_split(int batch, int num_kv_heads, int group, int max_seq_len, int k_b
   return true;
 }
 
+// Wave-private decode plan (tq_decode_wave.hip): each wave owns every KV head
+// of the page (num_kv_heads 1, 2 or 4, group <= 8) and loads whole pages
+// itself; the pages are split evenly over num_wg workgroups, one per CU (a
+// workgroup holds the CU's registers).  It beats the staged kernel where few
+// heads share a page (measured on the pages' geometry and the ragged batch);
+// with 8 heads a wave would hold 8 query groups and the staged kernel wins.
+// Returns false when the shape is outside this kernel's reach.
+struct WavePlan {
+  int nh;
+  int hsets;
+  int streams;
+  int num_wg;
+};
+
+// TQ_DECODE_KERNEL overrides the choice: "staged" (tq_decode.hip) or "wave"
+// (tq_decode_wave.hip, where the shape allows it); unset or "auto": the
+// planner's choice.
+int decode_kernel_choice() {
+  static const int choice = [] {
+    const char* e = std::getenv("TQ_DECODE_KERNEL");
+    if (!e || !*e || std::strcmp(e, "auto") == 0) return 0;
+    if (std::strcmp(e, "staged") == 0) return 1;
+    if (std::strcmp(e, "wave") == 0) return 2;
+    return 0;
+  }();
+  return choice;
+}
+
+bool plan_wave(int batch, int num_kv_heads, int group, int max_seq_len, int k_bits, int v_bits, int num_cus,
+               WavePlan* out) {
+  if (decode_kernel_choice() == 1 || group < 1 || group > 8) return false;
+  const long long max_pages = (max_seq_len + tq::kBlockSize - 1) / tq::kBlockSize;
+  if ((long long)batch * max_pages > (1LL << 40)) return false;
+  const int hkv = num_kv_heads;
+  if (hkv != 1 && hkv != 2 && hkv != 4) return false;
+  const int waves = tq::wave_waves(hkv);
+  if (waves == 0 || !tq::wave_fits(k_bits, v_bits, hkv, hkv)) return false;
+  WavePlan p;
+  p.nh = hkv;
+  p.hsets = 1;
+  p.streams = waves;
+  const long long units = std::max<long long>(1, (long long)batch * max_pages);
+  p.num_wg = (int)std::min<long long>(num_cus, units);
+  *out = p;
+  return true;
+}
+
+// The current device must be a gfx950; checked once per device.
+bool device_is_gfx950() {
+  static std::mutex mu;
+  static signed char cache[64] = {0};  // 0 unknown, 1 yes, -1 no
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return false;
+  if (dev >= 64) {
+    hipDeviceProp_t prop;
+    return hipGetDeviceProperties(&prop, dev) == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    const bool ok = hipGetDeviceProperties(&prop, dev) == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    cache[dev] = ok ? 1 : -1;
+  }
+  return cache[dev] > 0;
+}
+
 bool bits_ok(int b) { return b >= 2 && b <= 5; }
 
 }  // namespace
@@ -427,6 +493,7 @@ tq_status tq_write_kv(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype, in
   const tq_status st = make_write_args(ctx, raw, raw_dtype, num_tokens, num_kv_heads, pages, num_blocks,
                                        block_size, slots, bits, err_count, &a);
   if (st != TQ_OK || num_tokens == 0) return st;
+  if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
   return hip_status(tq::launch_write(a, (int)raw_dtype, bits, (hipStream_t)stream));
 }
 
@@ -442,6 +509,7 @@ tq_status tq_write_kv_pair(const tq_ctx* ctx, const void* raw_k, const void* raw
   st = make_write_args(ctx, raw_v, raw_dtype, num_tokens, num_kv_heads, v_pages, num_blocks, block_size,
                        slots, v_bits, nullptr, &v);
   if (st != TQ_OK || num_tokens == 0) return st;
+  if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
   return hip_status(tq::launch_write_pair(k, v, (int)raw_dtype, k_bits, v_bits, (hipStream_t)stream));
 }
 
@@ -461,7 +529,24 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads, 
         splits = p.num_splits;
     }
   size_t per = (size_t)batch * num_q_heads * splits;
+  // the wave-private kernel: one partial per (sequence, workgroup) pair it touches
+  const size_t wave_slots = (size_t)batch + (size_t)device_cu_count();
+  per = std::max(per, wave_slots * (size_t)num_q_heads);
   return per * (kHeadDim + 1) * sizeof(float) + 256;
+}
+
+const char* tq_decode_kernel(int batch, int num_q_heads, int num_kv_heads, int max_seq_len, int k_bits,
+                             int v_bits) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0 || num_q_heads % num_kv_heads ||
+      !bits_ok(k_bits) || !bits_ok(v_bits))
+    return nullptr;
+  const int group = num_q_heads / num_kv_heads;
+  if (group > tq::kMaxGroup) return nullptr;
+  WavePlan wp;
+  if (plan_wave(batch, num_kv_heads, group, max_seq_len, k_bits, v_bits, device_cu_count(), &wp)) return "wave";
+  SplitPlan p;
+  if (plan_split(batch, num_kv_heads, group, max_seq_len, k_bits, v_bits, device_cu_count(), &p)) return "staged";
+  return nullptr;
 }
 
 tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
@@ -489,14 +574,64 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
       tq_decode_workspace_bytes(ctx, batch, num_q_heads, num_kv_heads, max_seq_len, block_size);
   if (!workspace || workspace_bytes < need) return TQ_ERR_WORKSPACE;
 
-  SplitPlan p;
-  if (!plan_split(batch, num_kv_heads, group, max_seq_len, k_bits, v_bits, device_cu_count(), &p))
-    return TQ_ERR_UNSUPPORTED;
   const float sm_scale = scale > 0 ? scale : 1.0f / std::sqrt((float)kHeadDim);
   const float k_scale = ctx->tab_scale[k_bits];
   const float v_scale = ctx->tab_scale[v_bits];
   const int k_row_bytes = (int)tq_row_bytes(kHeadDim, k_bits);
   const int v_row_bytes = (int)tq_row_bytes(kHeadDim, v_bits);
+  const long long max_len_cap = std::min<long long>((long long)max_blocks_per_seq * block_size, 0x7fffffffLL);
+  if ((long long)block_size * num_kv_heads * std::max(k_row_bytes, v_row_bytes) > (1 << 30)) return TQ_ERR_UNSUPPORTED;
+
+  WavePlan wp;
+  if (plan_wave(batch, num_kv_heads, group, max_seq_len, k_bits, v_bits, device_cu_count(), &wp)) {
+    if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
+    tq::WaveArgs w;
+    std::memset(&w, 0, sizeof(w));
+    w.q = q;
+    w.k_pages = k_pages;
+    w.v_pages = v_pages;
+    w.block_table = block_table;
+    w.seq_lens = seq_lens;
+    w.part_acc = static_cast<float*>(workspace);
+    w.part_lse = w.part_acc + ((size_t)batch + wp.num_wg) * num_q_heads * kHeadDim;
+    w.k_page_bytes = (int64_t)block_size * num_kv_heads * k_row_bytes;
+    w.v_page_bytes = (int64_t)block_size * num_kv_heads * v_row_bytes;
+    w.num_blocks = num_blocks;
+    w.max_len = (int)max_len_cap;
+    w.batch = batch;
+    w.num_q_heads = num_q_heads;
+    w.num_kv_heads = num_kv_heads;
+    w.group = group;
+    w.max_blocks_per_seq = max_blocks_per_seq;
+    w.num_wg = wp.num_wg;
+    w.hsets = wp.hsets;
+    w.streams = wp.streams;
+    w.q_dtype = (int)q_dtype;
+    w.q_scale = (float)((double)sm_scale * 1.4426950408889634 / (std::sqrt((double)kHeadDim) * k_scale));
+    std::memcpy(w.sign_bits, ctx->sign_bits, sizeof(w.sign_bits));
+    for (int j = 0; j < (1 << k_bits); ++j) w.k_cent[j] = ctx->cent[k_bits][j] * k_scale;
+    for (int j = 0; j < (1 << v_bits); ++j) w.v_cent[j] = ctx->cent[v_bits][j] * v_scale;
+    tq_status st = hip_status(tq::launch_decode_wave(w, k_bits, v_bits, wp.nh, (hipStream_t)stream));
+    if (st != TQ_OK) return st;
+    tq::WaveMergeArgs m;
+    std::memset(&m, 0, sizeof(m));
+    m.part_acc = w.part_acc;
+    m.part_lse = w.part_lse;
+    m.seq_lens = seq_lens;
+    m.out = out;
+    m.batch = batch;
+    m.num_q_heads = num_q_heads;
+    m.num_wg = wp.num_wg;
+    m.max_len = w.max_len;
+    m.inv_v_scale_over_sqrt_d = (float)(1.0 / ((double)v_scale * std::sqrt((double)kHeadDim)));
+    std::memcpy(m.sign_bits, ctx->sign_bits, sizeof(m.sign_bits));
+    return hip_status(tq::launch_merge_wave(m, (hipStream_t)stream));
+  }
+
+  SplitPlan p;
+  if (!plan_split(batch, num_kv_heads, group, max_seq_len, k_bits, v_bits, device_cu_count(), &p))
+    return TQ_ERR_UNSUPPORTED;
+  if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
 
   tq::DecodeArgs d;
   std::memset(&d, 0, sizeof(d));

@@ -78,6 +78,58 @@ struct DecodeArgs {
   float v_cent[32];              // fp32 centroids of V times v_scale
 };
 
+// Arguments of the wave-private decode kernel (tq_decode_wave.hip).  The
+// pages of every sequence are concatenated in sequence order (sequence b
+// holds ceil(min(seq_lens[b], max_len) / 16) of them) and workgroup i of
+// num_wg takes pages [i T / num_wg, (i + 1) T / num_wg) of the T in total,
+// one sequence segment after the other.  Every wave of a workgroup owns all
+// KV heads (1, 2 or 4), loads whole pages with its own 16-byte loads into a
+// private LDS slot and computes every head's query group (group <= 8 query
+// heads per KV head); the waves of a workgroup (streams) walk alternate
+// pages of a segment and merge at its end.  Partial results of sequence b
+// from workgroup i go to workspace slot b + i.
+struct WaveArgs {
+  const void* q;                 // [B, Hq, 128]
+  const uint8_t* k_pages;
+  const uint8_t* v_pages;
+  const int32_t* block_table;    // [B, max_blocks_per_seq]
+  const int32_t* seq_lens;       // [B]
+  float* part_acc;               // [B + num_wg - 1, Hq, 128] rotated, normalised, x v_scale
+  float* part_lse;               // [B + num_wg - 1, Hq]      log2-sum-exp2 of the segment
+  int64_t k_page_bytes;
+  int64_t v_page_bytes;
+  int64_t num_blocks;            // block ids outside [0, num_blocks) read as zero rows
+  int32_t max_len;               // lengths are clamped to this (the block table's reach)
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;                 // num_q_heads / num_kv_heads (<= 8)
+  int32_t max_blocks_per_seq;
+  int32_t num_wg;                // workgroups of the launch
+  int32_t hsets;                 // head sets per workgroup (1: every wave owns every head)
+  int32_t streams;               // waves per head set
+  int32_t q_dtype;               // tq_dtype of q
+  float q_scale;                 // softmax scale * log2(e) / (sqrt(128) * k_scale)
+  uint32_t sign_bits[kHeadDim / 32];
+  float k_cent[32];              // fp32 centroids of K times k_scale
+  float v_cent[32];              // fp32 centroids of V times v_scale
+};
+
+// Arguments of the merge kernel of the wave-private decode: sequence b's
+// partials are the slots b + i of the workgroups i that took its pages.
+struct WaveMergeArgs {
+  const float* part_acc;
+  const float* part_lse;
+  const int32_t* seq_lens;
+  float* out;                    // [B, Hq, 128]
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_wg;
+  int32_t max_len;
+  float inv_v_scale_over_sqrt_d;
+  uint32_t sign_bits[kHeadDim / 32];
+};
+
 // Arguments of the split-merge + inverse-rotation kernel.
 struct MergeArgs {
   const float* part_acc;
@@ -101,5 +153,11 @@ hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, hipStream_
 int decode_table_bytes(int k_bits, int v_bits);  // LDS bytes of the decode lookup tables
 int decode_merge_lds_bytes();                     // LDS bytes of the stream merge
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+// wave-private decode: nh = KV heads per wave (1, 2 or 4); wave_fits is
+// false for any other nh and when the layout does not fit the CU's LDS
+bool wave_fits(int k_bits, int v_bits, int nh, int num_kv_heads);
+int wave_waves(int nh);                           // waves per workgroup (0: not built)
+hipError_t launch_decode_wave(const WaveArgs& a, int k_bits, int v_bits, int nh, hipStream_t stream);
+hipError_t launch_merge_wave(const WaveMergeArgs& a, hipStream_t stream);
 
 }  // namespace tq

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from paged_decode_attention_tq_amd import api, workloads
-from tests.parity import compare_decode
+from tests.parity import compare_decode, compare_pages
 
 pytestmark = pytest.mark.gpu
 
@@ -23,11 +23,13 @@ def ctx():
     return api.Context(128, 42)
 
 
-def _oracle_pipeline(w):
+def _oracle_pipeline(w, with_near=False):
     codec = oracle.OracleCodec(w.head_dim, w.rht_seed)
     kraw, vraw = w.rows("k"), w.rows("v")
-    kp, _ = codec.write_kv(kraw, w.zero_pages(w.k_bits), w.slots, w.k_bits)
-    vp, _ = codec.write_kv(vraw, w.zero_pages(w.v_bits), w.slots, w.v_bits)
+    kp, near_k = codec.write_kv(kraw, w.zero_pages(w.k_bits), w.slots, w.k_bits)
+    vp, near_v = codec.write_kv(vraw, w.zero_pages(w.v_bits), w.slots, w.v_bits)
+    if with_near:
+        return codec, kraw, vraw, kp, vp, near_k, near_v
     return codec, kraw, vraw, kp, vp
 
 
@@ -42,7 +44,7 @@ def _decode(ctx, w, q, kp, vp, scale=None):
 def _run(ctx, w, scale=None, q_dtype=None, gpu_write=True):
     print(f"[decode] {w.name} B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
           f"K{w.k_bits}V{w.v_bits} lens={w.seq_lens[:8].tolist()} scale={scale}", flush=True)
-    codec, kraw, vraw, kp, vp = _oracle_pipeline(w)
+    codec, kraw, vraw, kp, vp, near_k, near_v = _oracle_pipeline(w, with_near=True)
     q = w.queries()
     ref = oracle.paged_decode(q, kp, vp, w.block_table, w.seq_lens, w.k_bits, w.v_bits, codec.signs,
                               codec.centroids32(w.k_bits), codec.centroids32(w.v_bits), scale)
@@ -61,6 +63,10 @@ def _run(ctx, w, scale=None, q_dtype=None, gpu_write=True):
         slots = torch.from_numpy(w.slots).cuda()
         api.write_kv(ctx, torch.from_numpy(kraw).cuda(), kpg, slots, w.k_bits)
         api.write_kv(ctx, torch.from_numpy(vraw).cuda(), vpg, slots, w.v_bits)
+        # the GPU-written pages are the oracle's, byte for byte (near-boundary exemption)
+        written = int((w.slots >= 0).sum()) * w.num_kv_heads
+        compare_pages(kpg.cpu().numpy(), kp, near_k, w.k_bits, written)
+        compare_pages(vpg.cpu().numpy(), vp, near_v, w.v_bits, written)
         out2 = _decode(ctx, w, qt, kpg, vpg, scale)
         r2 = compare_decode(out2, ref, f"{w.name} gpu pages")
     print(f"  max|d| relL2 oracle-pages {r1}  gpu-pages {r2}", flush=True)

@@ -17,6 +17,21 @@ def test_splitmix64_published_outputs():
         assert oracle.splitmix64(v["seed"], len(want)) == want
 
 
+def test_signs_are_bit_63_of_the_published_outputs():
+    # the sign rule is pinned to the published generator outputs themselves
+    # (not to the oracle's own SplitMix64): s_i = -1 exactly when bit 63 of
+    # the i-th output is set; the vectors hold both signs
+    with open(golden_path("splitmix64_vectors.json")) as fh:
+        g = json.load(fh)
+    seen = set()
+    for v in g["vectors"]:
+        outs = [int(o, 0) for o in v["outputs"]]
+        want = np.array([-1 if (o >> 63) & 1 else 1 for o in outs], dtype=np.int8)
+        assert np.array_equal(oracle.rht_signs(v["seed"], len(outs)), want)
+        seen.update(want.tolist())
+    assert seen == {-1, 1}
+
+
 def test_signs_are_top_bits_and_balanced():
     s = oracle.rht_signs(42, 4096)
     assert set(np.unique(s)) == {-1, 1}

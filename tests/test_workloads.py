@@ -70,3 +70,33 @@ def test_mixed_bits_outlier_count():
     ch = np.abs(x).mean(axis=0)  # [Hkv, d]
     big = ch[w.outliers[:, 0], w.outliers[:, 1]]
     assert big.min() > 3 * np.median(ch)
+
+
+def test_chunked_oracle_helpers_equal_whole_sequence_oracle():
+    # the full-size checks run the oracle on 2048-token chunks in threads; the
+    # pieces put back together must be the oracle's whole-sequence result
+    import oracle
+    from tests import oracle_par
+
+    w = workloads.make_workload("chunks", k_bits=3, v_bits=4, num_q_heads=8, num_kv_heads=2,
+                                seq_lens=[5000, 37], seed=3, drop_frac=0.1)
+    codec = oracle.OracleCodec(128, 42)
+    q = w.queries()
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        npg = (L + 15) // 16
+        lo = int(w.cu_seqlens[b])
+        slots = np.where(w.slots[lo:lo + L] < 0, -1, np.arange(L)).astype(np.int64)
+        outs = {}
+        for comp, bits in (("k", w.k_bits), ("v", w.v_bits)):
+            whole, near = codec.write_kv(w.seq_rows(comp, b), np.zeros((npg, 16, 2, w.row_bytes(bits)), np.uint8),
+                                         slots, bits)
+            pages, near_c, kept = oracle_par.sequence_pages(codec, w, b, comp, bits)
+            assert np.array_equal(pages, whole) and np.array_equal(near_c, near)
+            assert kept == int((slots >= 0).sum())
+            outs[comp] = whole
+        ref = oracle.paged_decode_heads(q[b][None], outs["k"], outs["v"], np.arange(npg, dtype=np.int32)[None],
+                                        np.array([L]), w.k_bits, w.v_bits, codec.signs, codec.centroids32(w.k_bits),
+                                        codec.centroids32(w.v_bits), [(0, h) for h in range(8)])
+        got = oracle_par.sequence_outputs(codec, w, b, outs["k"], outs["v"], q)
+        assert np.array_equal(got, ref)
