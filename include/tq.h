@@ -192,6 +192,25 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype,
                           float* out, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* tq_paged_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same decode, arguments and results, with the split partials kept in a
+ * static scratch array of the library instead of a caller workspace.  Every
+ * GPU the library runs on holds its own 32 MiB copy of that array from module
+ * load until the process ends; the first call on a device looks its address
+ * up.  TQ_ERR_WORKSPACE, before any launch, when the sizes need more than
+ * 32 MiB (tq_decode_workspace_bytes > 32 MiB).  Calls that overlap on one GPU
+ * share the array and race; the caller orders them on one stream.  Nothing is
+ * allocated; asynchronous. */
+tq_status tq_paged_decode_noalloc(const tq_ctx* ctx, const void* q, tq_dtype q_dtype,
+                                  int batch, int num_q_heads, int num_kv_heads,
+                                  const uint8_t* k_pages, int k_bits,
+                                  const uint8_t* v_pages, int v_bits,
+                                  int64_t num_blocks, int block_size,
+                                  const int32_t* block_table, int max_blocks_per_seq,
+                                  const int32_t* seq_lens, int max_seq_len, float scale,
+                                  float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,13 @@ SIGNATURES = {
          _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_float,
          _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p],
     ),
+    "tq_paged_decode_noalloc": (
+        _c.c_int,
+        [_c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+         _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int,
+         _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_float,
+         _c.c_void_p, _c.c_void_p],
+    ),
 }
 
 

@@ -25,6 +25,7 @@ __all__ = [
     "decode_workspace_bytes",
     "decode_kernel",
     "paged_decode",
+    "paged_decode_noalloc",
 ]
 
 _DTYPES = {torch.float32: _lib.TQ_F32, torch.float16: _lib.TQ_F16, torch.bfloat16: _lib.TQ_BF16}
@@ -194,3 +195,32 @@ def paged_decode(ctx: Context, q: torch.Tensor, k_pages: torch.Tensor, v_pages: 
     check(st, "tq_paged_decode")
     return out
 
+
+def paged_decode_noalloc(ctx: Context, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                         block_table: torch.Tensor, seq_lens: torch.Tensor, k_bits: int, v_bits: int,
+                         max_seq_len: int | None = None, scale: float | None = None,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """``paged_decode`` without a workspace: the library's static scratch holds
+    the split partials (nothing is allocated when ``out`` is given)."""
+    _need(q.is_cuda and q.dim() == 3 and q.shape[2] == ctx.head_dim and q.is_contiguous(), "q must be [B, Hq, d]")
+    _need(q.dtype in _DTYPES, "q dtype must be fp32/fp16/bf16")
+    B, Hq, d = q.shape
+    for name, pg, bits in (("k_pages", k_pages, k_bits), ("v_pages", v_pages, v_bits)):
+        _need(pg.dtype == torch.uint8 and pg.dim() == 4 and pg.is_contiguous(), f"{name} must be uint8 4-D")
+        _need(pg.shape[3] == row_bytes(d, bits), f"{name} row_bytes does not match bits")
+    NB, BS, Hkv, _ = k_pages.shape
+    _need(tuple(v_pages.shape[:3]) == (NB, BS, Hkv), "k_pages / v_pages geometry mismatch")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B
+          and block_table.is_contiguous(), "block_table must be int32 [B, max_blocks]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (B,), "seq_lens must be int32 [B]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out.dtype == torch.float32 and out.shape == (B, Hq, d) and out.is_contiguous(), "out must be fp32 [B, Hq, d]")
+    st = _lib.lib().tq_paged_decode_noalloc(
+        ctx.handle, q.data_ptr(), _DTYPES[q.dtype], B, Hq, Hkv, k_pages.data_ptr(), k_bits,
+        v_pages.data_ptr(), v_bits, NB, BS, block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), max_seq_len, float(scale) if scale else 0.0, out.data_ptr(), _stream(q))
+    check(st, "tq_paged_decode_noalloc")
+    return out

@@ -704,4 +704,22 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   return hip_status(tq::launch_merge(m, (hipStream_t)stream));
 }
 
+tq_status tq_paged_decode_noalloc(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
+                                  int num_q_heads, int num_kv_heads, const uint8_t* k_pages, int k_bits,
+                                  const uint8_t* v_pages, int v_bits, int64_t num_blocks, int block_size,
+                                  const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                                  int max_seq_len, float scale, float* out, void* stream) {
+  if (!ctx || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return TQ_ERR_INVALID_ARG;
+  if (batch == 0) return TQ_OK;
+  const size_t need = tq_decode_workspace_bytes(ctx, batch, num_q_heads, num_kv_heads, max_seq_len, block_size);
+  if (need > tq::scratch_bytes()) return TQ_ERR_WORKSPACE;  // beyond the static scratch
+  if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
+  hipError_t e = hipSuccess;
+  void* ws = tq::scratch_device_ptr(&e);
+  if (!ws) return hip_status(e);
+  return tq_paged_decode(ctx, q, q_dtype, batch, num_q_heads, num_kv_heads, k_pages, k_bits, v_pages, v_bits,
+                         num_blocks, block_size, block_table, max_blocks_per_seq, seq_lens, max_seq_len, scale, out,
+                         ws, tq::scratch_bytes(), stream);
+}
+
 }  // extern "C"

@@ -160,4 +160,10 @@ int wave_waves(int nh);                           // waves per workgroup (0: not
 hipError_t launch_decode_wave(const WaveArgs& a, int k_bits, int v_bits, int nh, hipStream_t stream);
 hipError_t launch_merge_wave(const WaveMergeArgs& a, hipStream_t stream);
 
+// the static scratch of tq_paged_decode_noalloc (tq_scratch.hip): its size, and
+// its device address on the current device (looked up once per device; nullptr
+// and *err set when the lookup fails)
+size_t scratch_bytes();
+void* scratch_device_ptr(hipError_t* err);
+
 }  // namespace tq
