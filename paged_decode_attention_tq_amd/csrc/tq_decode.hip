@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     for (int j = 0; j < 32; ++j) x[j] = load_q(a.q, qoff + j, a.q_dtype);
 #pragma unroll
     for (int j = 0; j < 32; ++j) x[j] = has ? x[j] : 0.0f;
-    const uint32_t sw = a.sign_bits[c];
+    const uint32_t sw = pick4(a.sign_bits, c);
 #pragma unroll
     for (int j = 0; j < 32; ++j) x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((sw >> j) & 1u) << 31));
 #pragma unroll
@@ -771,8 +771,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     y0 = (lane & h) ? q0 - y0 : y0 + q0;
     y1 = (lane & h) ? q1 - y1 : y1 + q1;
   }
-  const float s0 = ((a.sign_bits[lane >> 5] >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
-  const float s1 = ((a.sign_bits[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
+  const float s0 = ((pick4(a.sign_bits, lane >> 5) >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
+  const float s1 = ((pick4(a.sign_bits, 2 + (lane >> 5)) >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
   o[lane] = s0 * y0 * a.inv_v_scale_over_sqrt_d;
   o[lane + 64] = s1 * y1 * a.inv_v_scale_over_sqrt_d;
 }

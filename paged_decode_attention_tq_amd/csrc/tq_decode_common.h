@@ -27,18 +27,30 @@ struct PairTable {
   static constexpr int kBytes = kRows * kStride;
 };
 
+// Centroid (lane & 31) of a kernel-argument table of 2^B entries (scalar
+// loads, as in pick4); the table fills gather from it with lane shuffles.
+template <int B>
+__device__ __forceinline__ float cent_of_lane(const float* cent, int lane) {
+  float v = 0.0f;
+#pragma unroll
+  for (int j = 0; j < (1 << B); ++j) v = ((lane & 31) == j) ? cent[j] : v;
+  return v;
+}
+
 template <int B>
 __device__ __forceinline__ void fill_pair_table(uint8_t* base, const float* cent, int tid, int nthreads) {
   using T = PairTable<B>;
   constexpr int kQuads = T::kBytes / 16;  // 2 replicas per 16-byte store
-  for (int i = tid; i < kQuads; i += nthreads) {
+  const float cl = cent_of_lane<B>(cent, tid & 63);
+  for (int i0 = 0; i0 < kQuads; i0 += nthreads) {  // every lane runs every round (shuffles)
+    const int i = min(i0 + tid, kQuads - 1);
     const int row = (2 * i) / T::kRep;
-    const float c0 = cent[row & ((1 << B) - 1)], c1 = cent[row >> B];
+    const float c0 = __shfl(cl, row & ((1 << B) - 1)), c1 = __shfl(cl, row >> B);
     const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
     const uint32_t hi = pack_half2(h0, h1);
     const uint32_t lo = pack_half2((_Float16)(c0 - (float)h0), (_Float16)(c1 - (float)h1));
     const bool swap = ((2 * i) % T::kRep) >= T::kRep / 2;
-    *reinterpret_cast<u32x4*>(base + 16 * i) = swap ? u32x4{lo, hi, lo, hi} : u32x4{hi, lo, hi, lo};
+    if (i0 + tid < kQuads) *reinterpret_cast<u32x4*>(base + 16 * i) = swap ? u32x4{lo, hi, lo, hi} : u32x4{hi, lo, hi, lo};
   }
 }
 
@@ -50,13 +62,15 @@ template <int B>
 __device__ __forceinline__ void fill_pair_table_flat(uint8_t* base, const float* cent, int tid, int nthreads) {
   using T = PairTable<B>;
   constexpr int kQuads = T::kBytes / 16;  // 2 replicas per 16-byte store
-  for (int i = tid; i < kQuads; i += nthreads) {
+  const float cl = cent_of_lane<B>(cent, tid & 63);
+  for (int i0 = 0; i0 < kQuads; i0 += nthreads) {  // every lane runs every round (shuffles)
+    const int i = min(i0 + tid, kQuads - 1);
     const int row = (2 * i) / T::kRep;
-    const float c0 = cent[row & ((1 << B) - 1)], c1 = cent[row >> B];
+    const float c0 = __shfl(cl, row & ((1 << B) - 1)), c1 = __shfl(cl, row >> B);
     const _Float16 h0 = (_Float16)c0, h1 = (_Float16)c1;
     const uint32_t hi = pack_half2(h0, h1);
     const uint32_t lo = pack_half2((_Float16)(c0 - (float)h0), (_Float16)(c1 - (float)h1));
-    *reinterpret_cast<u32x4*>(base + 16 * i) = u32x4{hi, lo, hi, lo};
+    if (i0 + tid < kQuads) *reinterpret_cast<u32x4*>(base + 16 * i) = u32x4{hi, lo, hi, lo};
   }
 }
 

@@ -26,7 +26,10 @@
 //    queries and lookup tables, staged through LDS) and at its end (the
 //    waves that walked the segment's pages merge through LDS); the segment's
 //    partial result of sequence b from workgroup i goes to workspace slot
-//    b + i, unique because workgroups take pages in order.
+//    b + i, unique because workgroups take pages in order.  A segment that
+//    is the whole sequence is finished on the spot (rotated back and written
+//    to out; the merge kernel skips it), and a launch of one workgroup needs
+//    no merge kernel at all.
 
 #include "tq_decode_common.h"
 
@@ -78,6 +81,14 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
   return v;
 }
 
+// floor(T i / n) for 0 <= i <= n (T, i, n wave-uniform): the boundaries of
+// the workgroups' shares.  32-bit division when T n fits in 32 bits (the
+// 64-bit one is a long software sequence on the critical path of both kernels).
+__device__ __forceinline__ long long share_point(long long T, long long i, long long n) {
+  if (T * n < (1LL << 32)) return (long long)((uint32_t)(T * i) / (uint32_t)n);
+  return T * i / n;
+}
+
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);
@@ -92,13 +103,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the fp16 hi part of query head x * group + n, column n + 8 its lo part;
 // qd[p] = the fp16 pair (dims 32c + 2p, 32c + 2p + 1) of the lane's column.
 // Scores come out multiplied by 1 / q_unscale, one power of two per group.
-__device__ __forceinline__ void rotate_query(const WaveArgs& a, int b, int x, int lane, uint32_t (&qd)[16],
-                                             float& q_unscale) {
+// load_query reads the lane's 32 query values (so that the loads can be in
+// flight while other work is issued), rotate_query forms qd from them.
+__device__ __forceinline__ void load_query(const WaveArgs& a, int b, int x, int lane, float (&v)[32]) {
   const int n = lane & 15, c = lane >> 4;
-  const int hq = n & 7, par = n >> 3;
+  const int hq = n & 7;
   const bool has = hq < a.group;
   const int64_t qoff = ((int64_t)b * a.num_q_heads + (int64_t)x * a.group + (has ? hq : 0)) * kHeadDim + 32 * c;
-  float v[32];
+  // (columns past the group read head 0's values; rotate_query zeroes them)
   if (a.q_dtype == 0) {
     const float* p = static_cast<const float*>(a.q) + qoff;
 #pragma unroll
@@ -112,9 +124,17 @@ __device__ __forceinline__ void rotate_query(const WaveArgs& a, int b, int x, in
 #pragma unroll
     for (int j = 0; j < 32; ++j) v[j] = bf16_to_f32(p[j]);
   }
+}
+
+__device__ __forceinline__ void rotate_query(const WaveArgs& a, int lane, float (&v)[32], uint32_t (&qd)[16],
+                                             float& q_unscale) {
+  const int n = lane & 15, c = lane >> 4;
+  const int par = n >> 3;
+  const bool has = (n & 7) < a.group;
 #pragma unroll
   for (int j = 0; j < 32; ++j) v[j] = has ? v[j] : 0.0f;
-  const uint32_t sw = a.sign_bits[c];
+  uint32_t sw = pick4(a.sign_bits, c);
+  asm volatile("" : "+v"(sw));  // keeps the 32 sign masks below from being hoisted (and held) out of the segment loop
 #pragma unroll
   for (int j = 0; j < 32; ++j) v[j] = __uint_as_float(__float_as_uint(v[j]) ^ (((sw >> j) & 1u) << 31));
 #pragma unroll
@@ -181,33 +201,44 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
   const int lane = tid & 63;
   const int n = lane & 15, c = lane >> 4;
   const int hq = n & 7, par = n >> 3;
-  const int S = a.streams;
-  const int hs = wave / S;
-  const int st = wave - hs * S;
-  const int g0 = hs * NH;  // first KV head of this wave
+  constexpr int S = W;     // streams: every wave owns every KV head and walks every W-th page
+  const int st = wave;
+  constexpr int g0 = 0;    // first KV head of this wave
   const int G = a.group;
   const int Hkv = a.num_kv_heads;
   const int B = a.batch;
 
   // ---- this workgroup's share of the pages ----------------------------------------
-  auto seq_pages = [&](int b) {
-    const int L = min(max(a.seq_lens[b], 0), a.max_len);
-    return (L + kBlockSize - 1) / kBlockSize;
-  };
+  auto seq_len = [&](int b) { return min(max(a.seq_lens[b], 0), a.max_len); };
+  auto pages_of = [](int L) { return (L + kBlockSize - 1) / kBlockSize; };
+  auto seq_pages = [&](int b) { return pages_of(seq_len(b)); };
+  // lengths of sequences base + lane (those of the first 64 are read once)
+  const int len_first = lane < B ? seq_len(lane) : 0;
+  auto len_at = [&](int base) { return base == 0 ? len_first : (base + lane < B ? seq_len(base + lane) : 0); };
   long long T = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int p = base + lane < B ? seq_pages(base + lane) : 0;
-    T += __builtin_amdgcn_readfirstlane(wave_sum_i(p));
+  for (int base = 0; base < B; base += 64) T += __builtin_amdgcn_readfirstlane(wave_sum_i(pages_of(len_at(base))));
+  const int Hq = a.num_q_heads;
+  if (a.direct) {
+    // no merge kernel follows: the one workgroup also writes the zero rows of
+    // empty sequences (one wave per sequence)
+    for (int bb = wave; bb < B; bb += W) {
+      if (seq_pages(bb) > 0) continue;
+      float* o = a.out + (int64_t)bb * Hq * kHeadDim;
+      for (int i = lane; i < Hq * kHeadDim / 4; i += 64)
+        *reinterpret_cast<floatx4*>(o + 4 * i) = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
   }
-  const long long r0 = T * wg / a.num_wg;
-  const long long r1 = T * (wg + 1) / a.num_wg;
+  const long long r0 = share_point(T, wg, a.num_wg);
+  const long long r1 = share_point(T, wg + 1, a.num_wg);
   if (r0 >= r1) return;  // every wave of the workgroup leaves here together
-  int b = 0;             // the sequence holding page r0, and its first page
+  int b = 0;             // the sequence holding page r0, its first page and its length
   long long sb = 0;
+  int L_cur = 0;
   {
     long long off = 0;
     for (int base = 0; base < B; base += 64) {
-      const int p = base + lane < B ? seq_pages(base + lane) : 0;
+      const int lv = len_at(base);
+      const int p = pages_of(lv);
       const int incl = wave_incl_scan(p, lane);
       const long long s_l = off + incl - p;
       const uint64_t hit = __ballot(p > 0 && s_l <= r0 && r0 < s_l + p);
@@ -215,6 +246,7 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
         const int l = __builtin_ctzll(hit);
         b = base + l;
         sb = off + __builtin_amdgcn_readlane(incl - p, l);
+        L_cur = __builtin_amdgcn_readlane(lv, l);
         break;
       }
       off += __builtin_amdgcn_readlane(incl, 63);
@@ -249,65 +281,37 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
   // ---- segments: the pages of one sequence inside this workgroup's share ------------
   bool first = true;
   while (sb < r1) {
-    const int L = min(max(a.seq_lens[b], 0), a.max_len);
-    const int pb = (L + kBlockSize - 1) / kBlockSize;
+    const int L = L_cur;
+    const int pb = pages_of(L);
     if (pb > 0) {
       const int ja = (int)((r0 > sb ? r0 : sb) - sb);
       const int je = (int)((r1 < sb + pb ? r1 : sb + pb) - sb);
-      if (!first) __syncthreads();  // the previous segment's merge is done with the LDS
-      first = false;
 
-      // -- rotated queries of every KV head, one head per wave at a time, staged in LDS
-      uint32_t* qst = reinterpret_cast<uint32_t*>(lds);
-      for (int x = wave; x < Hkv; x += W) {
-        uint32_t qx[16];
-        float qu;
-        rotate_query(a, b, x, lane, qx, qu);
-#pragma unroll
-        for (int p = 0; p < 16; ++p) qst[x * kQStageDwords + p * 64 + lane] = qx[p];
-        if (lane == 0) reinterpret_cast<float*>(qst)[Hkv * kQStageDwords + x] = qu;
-      }
-      __syncthreads();
-      uint32_t qd[NH][16];
-      float q_unscale[NH];
-#pragma unroll
-      for (int u = 0; u < NH; ++u) {
-#pragma unroll
-        for (int p = 0; p < 16; ++p) qd[u][p] = qst[(g0 + u) * kQStageDwords + p * 64 + lane];
-        q_unscale[u] = __int_as_float(
-            __builtin_amdgcn_readfirstlane(__float_as_int(reinterpret_cast<float*>(qst)[Hkv * kQStageDwords + g0 + u])));
-      }
-      __syncthreads();
-      fill_pair_table_flat<KB>(lds + LY::kKTab, a.k_cent, tid, 64 * W);
-      if constexpr (KB != VB) fill_pair_table_flat<VB>(lds + LY::kVTab, a.v_cent, tid, 64 * W);
-      __syncthreads();
-
-      // -- this wave's pages: segment pages ja + st, ja + st + S, ...
+      // -- loads first, in the order they are needed: this wave's block ids
+      // (its pages are segment pages ja + st, ja + st + S, ...), the query of
+      // its KV head (one head per wave: num_kv_heads <= 8 waves), then page 0,
+      // which is in flight while the query is rotated and the tables filled
       const int nseg = je - ja;
       const int n_my = nseg > st ? (nseg - st + S - 1) / S : 0;
       const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks_per_seq;
       auto bids_at = [&](int k0) {  // block ids of pages k0 .. k0 + 63, one per lane; -1: out of range
+        // (the read is unconditional, of an entry inside the sequence's row,
+        // so that it does not wait where it is issued)
         const int k = k0 + lane;
-        int v = -1;
-        if (k < n_my) {
-          const int x = bt[ja + st + k * S];
-          v = (x >= 0 && (int64_t)x < a.num_blocks) ? x : -1;
-        }
-        return v;
+        const int e = min(ja + st + min(k, max(n_my - 1, 0)) * S, a.max_blocks_per_seq - 1);
+        const int x = bt[e];
+        return (k < n_my && x >= 0 && (int64_t)x < a.num_blocks) ? x : -1;
       };
       int bid_cur = bids_at(0);
       int bid_next = bids_at(64);
 
-      floatx4 acc[NH][4];
-      float m_ref[NH], l_part[NH];
-#pragma unroll
-      for (int u = 0; u < NH; ++u) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[u][i] = floatx4{0.f, 0.f, 0.f, 0.f};
-        m_ref[u] = -__builtin_inff();
-        l_part[u] = 0.0f;
-      }
-
+      // (with four heads per wave the registers do not allow the query and
+      // page 0 to be held across the other loads and the barrier: they are
+      // loaded where they are used)
+      constexpr bool kEarly = NH <= 2;
+      float qraw[32];
+      const bool has_q = wave < Hkv;
+      if (kEarly && has_q) load_query(a, b, wave, lane, qraw);
       u32x4 R[MAXK + MAXV];
       auto issue = [&](int k) {  // page k's span into registers
         if ((k & 63) == 0 && k > 0) {
@@ -329,6 +333,46 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
         for (int i = 0; i < MAXV; ++i)
           R[MAXK + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16u * fold(i, VC), 0, kNT));
       };
+      if (kEarly && n_my > 0) issue(0);
+      if (!first) __syncthreads();  // the previous segment's merge is done with the LDS
+      first = false;
+
+      // -- rotated queries staged in LDS past the tables (in the page slots,
+      // which are not written before the next barrier), the tables meanwhile
+      uint32_t* qst = reinterpret_cast<uint32_t*>(lds + LY::kSlots);
+      if (has_q) {
+        uint32_t qx[16];
+        float qu;
+        if (!kEarly) load_query(a, b, wave, lane, qraw);
+        rotate_query(a, lane, qraw, qx, qu);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) qst[wave * kQStageDwords + p * 64 + lane] = qx[p];
+        if (lane == 0) reinterpret_cast<float*>(qst)[Hkv * kQStageDwords + wave] = qu;
+      }
+      fill_pair_table_flat<KB>(lds + LY::kKTab, a.k_cent, tid, 64 * W);
+      if constexpr (KB != VB) fill_pair_table_flat<VB>(lds + LY::kVTab, a.v_cent, tid, 64 * W);
+      __syncthreads();
+      uint32_t qd[NH][16];
+      float q_unscale[NH];
+#pragma unroll
+      for (int u = 0; u < NH; ++u) {
+#pragma unroll
+        for (int p = 0; p < 16; ++p) qd[u][p] = qst[(g0 + u) * kQStageDwords + p * 64 + lane];
+        q_unscale[u] = __int_as_float(
+            __builtin_amdgcn_readfirstlane(__float_as_int(reinterpret_cast<float*>(qst)[Hkv * kQStageDwords + g0 + u])));
+      }
+      __syncthreads();  // the staged queries are read: the slots may be written
+
+      floatx4 acc[NH][4];
+      float m_ref[NH], l_part[NH];
+#pragma unroll
+      for (int u = 0; u < NH; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[u][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        m_ref[u] = -__builtin_inff();
+        l_part[u] = 0.0f;
+      }
+
       auto commit = [&]() {  // the registers into the slot (in LDS order after the reads of the last page)
 #pragma unroll
         for (int i = 0; i < MAXK; ++i) *reinterpret_cast<u32x4*>(lds + slot + 16 * fold(i, KC)) = R[i];
@@ -498,7 +542,7 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
         });
       };
       if (n_my > 0) {
-        issue(0);
+        if (!kEarly) issue(0);
         commit();
         if (n_my > 1) issue(1);
       }
@@ -529,29 +573,12 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
         return lt;
       };
       const int64_t out_slot = (int64_t)b + wg;
-      const int Hq = a.num_q_heads;
-      if (S == 1) {
-#pragma unroll
-        for (int u = 0; u < NH; ++u) {
-          float o[4][8];
-          const float lt = finish_head(u, o);
-          if (par == 0 && hq < G) {
-            const int h = (g0 + u) * G + hq;
-            const float inv = 1.0f / lt;
-            float* dst = a.part_acc + (out_slot * Hq + h) * kHeadDim + 32 * c;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              *reinterpret_cast<floatx4*>(dst + 8 * r) =
-                  floatx4{o[r][0] * inv, o[r][1] * inv, o[r][2] * inv, o[r][3] * inv};
-              *reinterpret_cast<floatx4*>(dst + 8 * r + 4) =
-                  floatx4{o[r][4] * inv, o[r][5] * inv, o[r][6] * inv, o[r][7] * inv};
-            }
-            if (c == 0) a.part_lse[out_slot * Hq + h] = m_ref[u] + __builtin_log2f(lt);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-        // the streams of each head set merge through LDS (slots and tables are dead)
+      // this workgroup holds every page of the sequence: it writes the final
+      // output (normalised, rotated back, value scale divided out) and the
+      // merge kernel skips the sequence
+      const bool whole = ja == 0 && je == pb;
+      {
+        // the W streams merge through LDS (slots and tables are dead)
         __syncthreads();
         constexpr int kRow = LY::kMergeRow;
         float* mg = reinterpret_cast<float*>(lds);
@@ -589,6 +616,7 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
             float ov[16];
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) ov[jj] = 0.0f;
+#pragma unroll 2
             for (int t = 0; t < S; ++t) {
               const int e = ((hsx * S + t) * NH + ux) * 8 + hh;
               const float mt = m_buf[e];
@@ -606,25 +634,65 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
             }
             const float inv = 1.0f / lsum;
             const int h = x * G + hh;
-            float* dst = a.part_acc + (out_slot * Hq + h) * kHeadDim + d0;
+            if (whole) {
+              // y = H (ov / l) over the 128 dims d0 + jj = 16 (lane & 7) + jj
+              // (the unnormalised Hadamard butterfly: dims i < j = i + step
+              // become (y_i + y_j, y_i - y_j)): steps 1 .. 8 inside the lane,
+              // 16 .. 64 across the head's eight lanes; then the signs and the
+              // value scale with the rotation's 1 / sqrt(128)
+              float y[16];
 #pragma unroll
-            for (int jj = 0; jj < 16; jj += 4)
-              *reinterpret_cast<floatx4*>(dst + jj) = floatx4{ov[jj] * inv, ov[jj + 1] * inv, ov[jj + 2] * inv, ov[jj + 3] * inv};
-            if ((lane & 7) == 0) a.part_lse[out_slot * Hq + h] = M + __builtin_log2f(lsum);
+              for (int jj = 0; jj < 16; ++jj) y[jj] = ov[jj] * inv;
+#pragma unroll
+              for (int st2 = 1; st2 < 16; st2 <<= 1)
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj)
+                  if ((jj & st2) == 0) {
+                    const float u0 = y[jj], u1 = y[jj + st2];
+                    y[jj] = u0 + u1;
+                    y[jj + st2] = u0 - u1;
+                  }
+#pragma unroll
+              for (int lb = 1; lb < 8; lb <<= 1)
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                  const float pv = __shfl_xor(y[jj], lb);
+                  y[jj] = (lane & lb) ? pv - y[jj] : y[jj] + pv;
+                }
+              uint32_t sw = pick4(a.sign_bits, d0 >> 5) >> (d0 & 31);  // the 16 signs of dims d0 .. d0 + 15
+              asm volatile("" : "+v"(sw));  // (computed here, not hoisted and held across the walk)
+              float* dst = a.out + ((int64_t)b * Hq + h) * kHeadDim + d0;
+#pragma unroll
+              for (int jj = 0; jj < 16; jj += 4) {
+                floatx4 o4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  o4[e] = (((sw >> (jj + e)) & 1u) ? -a.out_scale : a.out_scale) * y[jj + e];
+                *reinterpret_cast<floatx4*>(dst + jj) = o4;
+              }
+            } else {
+              float* dst = a.part_acc + (out_slot * Hq + h) * kHeadDim + d0;
+#pragma unroll
+              for (int jj = 0; jj < 16; jj += 4)
+                *reinterpret_cast<floatx4*>(dst + jj) =
+                    floatx4{ov[jj] * inv, ov[jj + 1] * inv, ov[jj + 2] * inv, ov[jj + 3] * inv};
+              if ((lane & 7) == 0) a.part_lse[out_slot * Hq + h] = M + __builtin_log2f(lsum);
+            }
           }
         }
       }
     }
     sb += pb;
     ++b;
+    if (sb < r1) L_cur = seq_len(b);
   }
 }
 
 template <int KB, int VB, int NH>
 static constexpr bool wave_layout_fits(int num_kv_heads) {
   using LY = WaveLayout<KB, VB, NH>;
-  return LY::kBytes <= kDecodeLdsBytes && LY::kMergeBytes <= kDecodeLdsBytes &&
-         num_kv_heads * (kQStageDwords * 4 + 4) <= kDecodeLdsBytes;
+  return LY::kBytes <= kDecodeLdsBytes && LY::kMergeBytes <= kDecodeLdsBytes && num_kv_heads <= LY::kW &&
+         num_kv_heads * (kQStageDwords * 4 + 4) <= LY::kW * LY::kSlot;
 }
 
 template <int KB, int VB>
@@ -706,8 +774,9 @@ hipError_t launch_decode_wave(const WaveArgs& a, int k_bits, int v_bits, int nh,
 // ===========================================================================
 // Merge: one wave per (b, h).  Finds the workgroups that took sequence b's
 // pages (the same integer split of the page concatenation as the decode
-// kernel), combines their normalised rotated sums by their log2-sum-exp2,
-// divides the value scale out, applies the inverse rotation
+// kernel); a sequence that one workgroup held was finished there.  Otherwise
+// it combines the workgroups' normalised rotated sums by their
+// log2-sum-exp2, divides the value scale out, applies the inverse rotation
 // s * H y / sqrt(128) and writes fp32 out.  Lane l owns dims l and l + 64.
 // ===========================================================================
 __global__ __launch_bounds__(256) void merge_wave_kernel(WaveMergeArgs a) {
@@ -738,16 +807,17 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(WaveMergeArgs a) {
   }
   const long long NW = a.num_wg;
   auto wg_of = [&](long long page) {  // the workgroup i with i T / NW <= page < (i + 1) T / NW
-    long long i = page * NW / T;
-    while (i + 1 < NW && (i + 1) * T / NW <= page) ++i;
-    while (i > 0 && i * T / NW > page) --i;
+    long long i = T * NW < (1LL << 32) ? (long long)((uint32_t)(page * NW) / (uint32_t)T) : page * NW / T;
+    while (i + 1 < NW && share_point(T, i + 1, NW) <= page) ++i;
+    while (i > 0 && share_point(T, i, NW) > page) --i;
     return (int)i;
   };
   const int i0 = wg_of(sb), i1 = wg_of(sb + pb - 1);
+  if (i0 == i1) return;  // one workgroup held the whole sequence and wrote its output
   const int ns = i1 - i0 + 1;
   // a workgroup between i0 and i1 whose share is empty (more workgroups than
   // pages) wrote nothing: its slot is skipped
-  auto live = [&](int i) { return (long long)i * T / NW < (long long)(i + 1) * T / NW; };
+  auto live = [&](int i) { return share_point(T, i, NW) < share_point(T, i + 1, NW); };
   const int64_t slot0 = (int64_t)b + i0;
   const float* lse = a.part_lse + slot0 * Hq + h;                      // stride Hq per slot
   const float* pa = a.part_acc + (slot0 * Hq + h) * kHeadDim;          // stride Hq * 128 per slot
@@ -766,14 +836,15 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(WaveMergeArgs a) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off);
     den += ws;
-    int u = 0;
-    constexpr int kU = 16;  // 16 slots per round: all their loads in flight together
-    // (a slot of weight 0 is not read: it may be an empty workgroup's)
-    for (; u + kU <= cnt; u += kU) {
+    // rounds of 8 slots with all their loads in flight together; a slot past
+    // the end or of weight 0 is not read (it may be an empty workgroup's)
+    constexpr int kU = 8;
+    for (int u = 0; u < cnt; u += kU) {
       float v0[kU], v1[kU], wu[kU];
 #pragma unroll
       for (int q = 0; q < kU; ++q) {
-        wu[q] = __shfl(wgt, u + q);
+        const float wq = __shfl(wgt, min(u + q, 63));
+        wu[q] = u + q < cnt ? wq : 0.0f;
         const int64_t at = (int64_t)(s0 + u + q) * pstride;
         v0[q] = wu[q] != 0.0f ? pa[at + lane] : 0.0f;
         v1[q] = wu[q] != 0.0f ? pa[at + lane + 64] : 0.0f;
@@ -782,13 +853,6 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(WaveMergeArgs a) {
       for (int q = 0; q < kU; ++q) {
         y0 += wu[q] * v0[q];
         y1 += wu[q] * v1[q];
-      }
-    }
-    for (; u < cnt; ++u) {
-      const float wv = __shfl(wgt, u);
-      if (wv != 0.0f) {
-        y0 += wv * pa[(int64_t)(s0 + u) * pstride + lane];
-        y1 += wv * pa[(int64_t)(s0 + u) * pstride + lane + 64];
       }
     }
   }
@@ -807,8 +871,8 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(WaveMergeArgs a) {
     y0 = (lane & hh) ? q0 - y0 : y0 + q0;
     y1 = (lane & hh) ? q1 - y1 : y1 + q1;
   }
-  const float s0 = ((a.sign_bits[lane >> 5] >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
-  const float s1 = ((a.sign_bits[2 + (lane >> 5)] >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
+  const float s0 = ((pick4(a.sign_bits, lane >> 5) >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
+  const float s1 = ((pick4(a.sign_bits, 2 + (lane >> 5)) >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
   o[lane] = s0 * y0 * a.inv_v_scale_over_sqrt_d;
   o[lane + 64] = s1 * y1 * a.inv_v_scale_over_sqrt_d;
 }

@@ -56,6 +56,14 @@ __device__ __forceinline__ double sqrt_rn(double S) {
 }
 
 
+// Word idx (0..3) of a four-word kernel-argument array.  The words come from
+// scalar loads at fixed offsets: indexing the array with a per-lane value
+// would read the argument segment with vector loads, one wait each.
+__device__ __forceinline__ uint32_t pick4(const uint32_t* w, int idx) {
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+  return (idx & 2) ? ((idx & 1) ? w3 : w2) : ((idx & 1) ? w1 : w0);
+}
+
 __device__ __forceinline__ uint32_t pack_half2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }

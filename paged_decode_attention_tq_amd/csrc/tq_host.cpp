@@ -323,11 +323,14 @@ bool plan_split(int batch, int num_kv_heads, int group, int max_seq_len, int k_b
 // workgroup holds the CU's registers).  It beats the staged kernel where few
 // heads share a page (measured on the pages' geometry and the ragged batch);
 // with 8 heads a wave would hold 8 query groups and the staged kernel wins.
+// A small batch (at most kDirectPages pages in all, at most 64 sequences)
+// runs as one workgroup, which finishes every sequence itself: no merge
+// kernel, whose launch and dependent loads cost more than a few pages.
 // Returns false when the shape is outside this kernel's reach.
+constexpr long long kDirectPages = 32;  // four pages per wave of the one workgroup
+
 struct WavePlan {
-  int nh;
-  int hsets;
-  int streams;
+  int nh;      // KV heads per wave (all of the page's)
   int num_wg;
 };
 
@@ -356,10 +359,8 @@ bool plan_wave(int batch, int num_kv_heads, int group, int max_seq_len, int k_bi
   if (waves == 0 || !tq::wave_fits(k_bits, v_bits, hkv, hkv)) return false;
   WavePlan p;
   p.nh = hkv;
-  p.hsets = 1;
-  p.streams = waves;
   const long long units = std::max<long long>(1, (long long)batch * max_pages);
-  p.num_wg = (int)std::min<long long>(num_cus, units);
+  p.num_wg = (units <= kDirectPages && batch <= 64) ? 1 : (int)std::min<long long>(num_cus, units);
   *out = p;
   return true;
 }
@@ -594,6 +595,8 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
     w.seq_lens = seq_lens;
     w.part_acc = static_cast<float*>(workspace);
     w.part_lse = w.part_acc + ((size_t)batch + wp.num_wg) * num_q_heads * kHeadDim;
+    w.out = out;
+    w.direct = wp.num_wg == 1 ? 1 : 0;  // then every sequence is finished by the decode kernel
     w.k_page_bytes = (int64_t)block_size * num_kv_heads * k_row_bytes;
     w.v_page_bytes = (int64_t)block_size * num_kv_heads * v_row_bytes;
     w.num_blocks = num_blocks;
@@ -604,15 +607,14 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
     w.group = group;
     w.max_blocks_per_seq = max_blocks_per_seq;
     w.num_wg = wp.num_wg;
-    w.hsets = wp.hsets;
-    w.streams = wp.streams;
     w.q_dtype = (int)q_dtype;
     w.q_scale = (float)((double)sm_scale * 1.4426950408889634 / (std::sqrt((double)kHeadDim) * k_scale));
+    w.out_scale = (float)(1.0 / ((double)v_scale * std::sqrt((double)kHeadDim)));
     std::memcpy(w.sign_bits, ctx->sign_bits, sizeof(w.sign_bits));
     for (int j = 0; j < (1 << k_bits); ++j) w.k_cent[j] = ctx->cent[k_bits][j] * k_scale;
     for (int j = 0; j < (1 << v_bits); ++j) w.v_cent[j] = ctx->cent[v_bits][j] * v_scale;
     tq_status st = hip_status(tq::launch_decode_wave(w, k_bits, v_bits, wp.nh, (hipStream_t)stream));
-    if (st != TQ_OK) return st;
+    if (st != TQ_OK || w.direct) return st;
     tq::WaveMergeArgs m;
     std::memset(&m, 0, sizeof(m));
     m.part_acc = w.part_acc;
@@ -623,7 +625,7 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
     m.num_q_heads = num_q_heads;
     m.num_wg = wp.num_wg;
     m.max_len = w.max_len;
-    m.inv_v_scale_over_sqrt_d = (float)(1.0 / ((double)v_scale * std::sqrt((double)kHeadDim)));
+    m.inv_v_scale_over_sqrt_d = w.out_scale;
     std::memcpy(m.sign_bits, ctx->sign_bits, sizeof(m.sign_bits));
     return hip_status(tq::launch_merge_wave(m, (hipStream_t)stream));
   }

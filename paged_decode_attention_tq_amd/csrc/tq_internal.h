@@ -87,7 +87,8 @@ struct DecodeArgs {
 // private LDS slot and computes every head's query group (group <= 8 query
 // heads per KV head); the waves of a workgroup (streams) walk alternate
 // pages of a segment and merge at its end.  Partial results of sequence b
-// from workgroup i go to workspace slot b + i.
+// from workgroup i go to workspace slot b + i; a sequence whose pages all
+// fall in one workgroup's share is finished by that workgroup (out).
 struct WaveArgs {
   const void* q;                 // [B, Hq, 128]
   const uint8_t* k_pages;
@@ -96,6 +97,7 @@ struct WaveArgs {
   const int32_t* seq_lens;       // [B]
   float* part_acc;               // [B + num_wg - 1, Hq, 128] rotated, normalised, x v_scale
   float* part_lse;               // [B + num_wg - 1, Hq]      log2-sum-exp2 of the segment
+  float* out;                    // [B, Hq, 128]: written here for every sequence whose pages one workgroup holds
   int64_t k_page_bytes;
   int64_t v_page_bytes;
   int64_t num_blocks;            // block ids outside [0, num_blocks) read as zero rows
@@ -106,17 +108,18 @@ struct WaveArgs {
   int32_t group;                 // num_q_heads / num_kv_heads (<= 8)
   int32_t max_blocks_per_seq;
   int32_t num_wg;                // workgroups of the launch
-  int32_t hsets;                 // head sets per workgroup (1: every wave owns every head)
-  int32_t streams;               // waves per head set
   int32_t q_dtype;               // tq_dtype of q
+  int32_t direct;                // 1: no merge kernel follows (one workgroup): empty sequences are zeroed here too
   float q_scale;                 // softmax scale * log2(e) / (sqrt(128) * k_scale)
+  float out_scale;               // 1 / (v_scale * sqrt(128)): value scale and the rotation's normalisation
   uint32_t sign_bits[kHeadDim / 32];
   float k_cent[32];              // fp32 centroids of K times k_scale
   float v_cent[32];              // fp32 centroids of V times v_scale
 };
 
 // Arguments of the merge kernel of the wave-private decode: sequence b's
-// partials are the slots b + i of the workgroups i that took its pages.
+// partials are the slots b + i of the workgroups i that took its pages; a
+// sequence whose pages one workgroup took was finished by the decode kernel.
 struct WaveMergeArgs {
   const float* part_acc;
   const float* part_lse;

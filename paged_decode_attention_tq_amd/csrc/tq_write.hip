@@ -66,14 +66,15 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, int64_t wg) {
   const int64_t tok = row / a.num_kv_heads;
   const int head = (int)(row - tok * a.num_kv_heads);
   const int64_t slot = a.slots[tok];
+  // the row is read before its slot is known (both loads in flight
+  // together); a dropped row's read is wasted
+  float x[32];
+  load_row32<DT>(a.raw, row * kHeadDim + 32 * q, x);
   if (slot < 0) return;
   if (slot >= a.num_slots) {
     if (q == 0 && head == 0 && a.err_count) atomicAdd(a.err_count, 1);
     return;
   }
-
-  float x[32];
-  load_row32<DT>(a.raw, row * kHeadDim + 32 * q, x);
 
   // ---- norm: float64 sum of squares, exact-rounded ------------------------
   double s = 0.0;
@@ -114,7 +115,7 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, int64_t wg) {
   const float c = n64 > 0.0 ? (float)(1.0 / (n64 * 11.313708498984761)) : 0.0f;  // 1/(n sqrt(128))
 
   // ---- randomized Hadamard transform ------------------------------------
-  const uint32_t sw = a.sign_bits[q];
+  const uint32_t sw = pick4(a.sign_bits, q);
 #pragma unroll
   for (int j = 0; j < 32; ++j) x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((sw >> j) & 1u) << 31));
 #pragma unroll
