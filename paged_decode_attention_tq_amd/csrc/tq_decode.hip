@@ -252,15 +252,9 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
           x[j + h] = u - v;
         }
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float p = __shfl_xor(x[j], 16);
-      x[j] = (c & 1) ? p - x[j] : x[j] + p;
-    }
+    for (int j = 0; j < 32; ++j) x[j] = lane_bfly<16>(x[j], lane);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float p = __shfl_xor(x[j], 32);
-      x[j] = (c & 2) ? p - x[j] : x[j] + p;
-    }
+    for (int j = 0; j < 32; ++j) x[j] = lane_bfly<32>(x[j], lane);
     // power-of-two scale that puts the wave's largest coordinate near 2^10,
     // so the fp16 hi/lo halves keep their precision for any query magnitude
     float amax = 0.0f;
@@ -765,12 +759,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     y0 = u + v;
     y1 = u - v;
   }
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const float q0 = __shfl_xor(y0, h), q1 = __shfl_xor(y1, h);
-    y0 = (lane & h) ? q0 - y0 : y0 + q0;
-    y1 = (lane & h) ? q1 - y1 : y1 + q1;
-  }
+  static_for<6>([&](auto sc) {
+    constexpr int M = 1 << decltype(sc)::value;
+    y0 = lane_bfly<M>(y0, lane);
+    y1 = lane_bfly<M>(y1, lane);
+  });
   const float s0 = ((pick4(a.sign_bits, lane >> 5) >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
   const float s1 = ((pick4(a.sign_bits, 2 + (lane >> 5)) >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
   o[lane] = s0 * y0 * a.inv_v_scale_over_sqrt_d;

@@ -6,6 +6,9 @@
 #include "tq_internal.h"
 #include "tq_device.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace tq {
 
 // ---------------------------------------------------------------------------
@@ -129,6 +132,44 @@ __device__ __forceinline__ float max_across_rows(float v) {
 
 __device__ __forceinline__ float row_ror8(float v) {  // lane n <-> n ^ 8 inside a 16-lane row
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
+// f(integral_constant<0>), ..., f(integral_constant<N - 1>)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Hadamard butterfly between lanes l and l ^ M: lanes with bit M clear get
+// x_l + x_(l^M), the others x_(l^M) - x_l.  M = 16, 32: one permlane swap
+// (both copies of x in, partner and self out) and one FMA with sign +-1
+// (exact: the same rounding as the add or subtract); M = 1, 2: DPP quad
+// permutes; M = 4, 8: LDS-free swizzle / row rotate.
+template <int M>
+__device__ __forceinline__ float lane_bfly(float x, int lane) {
+  const bool upper = (lane & M) != 0;
+  if constexpr (M == 16 || M == 32) {
+    // the swap puts self in [0] and the partner in [1] on lanes with bit M
+    // clear, partner in [0] and self in [1] on the others
+    const auto s = M == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                           : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaf(upper ? -1.0f : 1.0f, __uint_as_float(s[1]), __uint_as_float(s[0]));
+  } else {
+    float p;
+    if constexpr (M == 1)
+      p = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    else if constexpr (M == 2)
+      p = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    else if constexpr (M == 8)
+      p = row_ror8(x);
+    else
+      p = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (M << 10)));  // lane ^ M within 32
+    return upper ? p - x : x + p;
+  }
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));

@@ -89,15 +89,6 @@ __device__ __forceinline__ long long share_point(long long T, long long i, long 
   return T * i / n;
 }
 
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 // Rotated, scaled query of KV head x's query group as the B operand of the
 // score MFMAs.  Lane (n, c) covers dims 32c .. 32c + 31; column n < 8 holds
 // the fp16 hi part of query head x * group + n, column n + 8 its lo part;
@@ -147,15 +138,9 @@ __device__ __forceinline__ void rotate_query(const WaveArgs& a, int lane, float 
         v[j + h] = u - w;
       }
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float p = __shfl_xor(v[j], 16);
-    v[j] = (c & 1) ? p - v[j] : v[j] + p;
-  }
+  for (int j = 0; j < 32; ++j) v[j] = lane_bfly<16>(v[j], lane);
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float p = __shfl_xor(v[j], 32);
-    v[j] = (c & 2) ? p - v[j] : v[j] + p;
-  }
+  for (int j = 0; j < 32; ++j) v[j] = lane_bfly<32>(v[j], lane);
   // one power of two for the group that puts its largest coordinate near 2^10,
   // so the fp16 hi / lo halves keep their precision for any query magnitude
   float amax = 0.0f;
@@ -652,13 +637,10 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
                     y[jj] = u0 + u1;
                     y[jj + st2] = u0 - u1;
                   }
+              static_for<3>([&](auto sc) {
 #pragma unroll
-              for (int lb = 1; lb < 8; lb <<= 1)
-#pragma unroll
-                for (int jj = 0; jj < 16; ++jj) {
-                  const float pv = __shfl_xor(y[jj], lb);
-                  y[jj] = (lane & lb) ? pv - y[jj] : y[jj] + pv;
-                }
+                for (int jj = 0; jj < 16; ++jj) y[jj] = lane_bfly<(1 << decltype(sc)::value)>(y[jj], lane);
+              });
               uint32_t sw = pick4(a.sign_bits, d0 >> 5) >> (d0 & 31);  // the 16 signs of dims d0 .. d0 + 15
               asm volatile("" : "+v"(sw));  // (computed here, not hoisted and held across the walk)
               float* dst = a.out + ((int64_t)b * Hq + h) * kHeadDim + d0;
@@ -822,15 +804,17 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(WaveMergeArgs a) {
   const float* lse = a.part_lse + slot0 * Hq + h;                      // stride Hq per slot
   const float* pa = a.part_acc + (slot0 * Hq + h) * kHeadDim;          // stride Hq * 128 per slot
   const int64_t pstride = (int64_t)Hq * kHeadDim;
-  float M = -__builtin_inff();
-  for (int s = lane; s < ns; s += 64)
-    if (live(i0 + s)) M = fmaxf(M, lse[(int64_t)s * Hq]);
+  // lane s holds slot s's log2-sum-exp2 (the first 64 slots are read once)
+  auto lse_at = [&](int s) { return (s < ns && live(i0 + s)) ? lse[(int64_t)s * Hq] : -__builtin_inff(); };
+  const float lse_first = lse_at(lane);
+  float M = lse_first;
+  for (int s = lane + 64; s < ns; s += 64) M = fmaxf(M, lse_at(s));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float den = 0.0f, y0 = 0.0f, y1 = 0.0f;
   for (int s0 = 0; s0 < ns; s0 += 64) {
     const int cnt = min(64, ns - s0);
-    const float my = (lane < cnt && live(i0 + s0 + lane)) ? lse[(int64_t)(s0 + lane) * Hq] : -__builtin_inff();
+    const float my = s0 == 0 ? lse_first : lse_at(s0 + lane);
     const float wgt = (my == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(my - M);
     float ws = wgt;
 #pragma unroll
@@ -865,12 +849,11 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(WaveMergeArgs a) {
     y0 = u + v;
     y1 = u - v;
   }
-#pragma unroll
-  for (int hh = 1; hh < 64; hh <<= 1) {
-    const float q0 = __shfl_xor(y0, hh), q1 = __shfl_xor(y1, hh);
-    y0 = (lane & hh) ? q0 - y0 : y0 + q0;
-    y1 = (lane & hh) ? q1 - y1 : y1 + q1;
-  }
+  static_for<6>([&](auto sc) {
+    constexpr int M = 1 << decltype(sc)::value;
+    y0 = lane_bfly<M>(y0, lane);
+    y1 = lane_bfly<M>(y1, lane);
+  });
   const float s0 = ((pick4(a.sign_bits, lane >> 5) >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
   const float s1 = ((pick4(a.sign_bits, 2 + (lane >> 5)) >> (lane & 31)) & 1u) ? -1.0f : 1.0f;
   o[lane] = s0 * y0 * a.inv_v_scale_over_sqrt_d;
