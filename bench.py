@@ -94,21 +94,20 @@ def cpu_baseline(w, kraw, vraw, q, seconds=15.0):
     }
 
 
-def traffic_bytes():
-    """HBM bytes per decode call from the committed counter profile, if it was
-    taken on the current decode source (else None)."""
+def traffic_bytes(config):
+    """HBM bytes per decode call of this config from the committed counter
+    profile, if it was taken on the current decode sources (else None)."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
-    src = os.path.join(ROOT, "paged_decode_attention_tq_amd", "csrc", "tq_decode.hip")
     try:
         prof = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except (OSError, ValueError):
+        digest = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in prof["sources"])).hexdigest()
+    except (OSError, ValueError, KeyError, TypeError):
         return None
-    if prof.get("tq_decode_hip_sha256") != digest:
+    if prof.get("decode_sources_sha256") != digest:
         return None
-    return prof.get("bytes_per_call")
+    return prof.get("configs", {}).get(config, {}).get("bytes_per_call")
 
 
 def main():
@@ -243,7 +242,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic_bytes(),
+            "traffic": traffic_bytes(w.name),
         },
         "cpu_baseline": None,
     }
