@@ -237,7 +237,8 @@ def main():
         "context_tokens_per_s": float(w.num_tokens) / dec_s,
         "roofline": {
             "bound": "hbm",
-            "kernel": f"tq_paged_decode, {kernel} decode kernel + merge kernel",
+            "kernel": (f"tq_paged_decode, {kernel} decode kernel + merge kernel" if kernel != "wave1" else
+                       "tq_paged_decode, wave decode kernel as one workgroup (no merge kernel)"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

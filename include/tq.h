@@ -150,9 +150,11 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
 
 /* Which decode kernel tq_paged_decode runs for these sizes on the current
  * device: "wave" (every wave owns all KV heads and walks its own pages;
- * 1, 2 or 4 KV heads with at most 8 query heads each), "staged" (a
- * workgroup stages whole pages for all its waves), or NULL when the sizes are
- * not supported.  The environment variable TQ_DECODE_KERNEL=staged|wave
+ * 1, 2 or 4 KV heads with at most 8 query heads each), "wave1" (the same
+ * kernel as one workgroup that finishes every sequence itself, with no merge
+ * kernel: at most 32 pages in all and 64 sequences), "staged" (a workgroup
+ * stages whole pages for all its waves), or NULL when the sizes are not
+ * supported.  The environment variable TQ_DECODE_KERNEL=staged|wave
  * overrides the choice where the sizes allow it.  Host-only; static string. */
 const char* tq_decode_kernel(int batch, int num_q_heads, int num_kv_heads,
                              int max_seq_len, int k_bits, int v_bits);

@@ -155,7 +155,8 @@ def decode_workspace_bytes(ctx: Context, batch, num_q_heads, num_kv_heads, max_s
 
 
 def decode_kernel(batch, num_q_heads, num_kv_heads, max_seq_len, k_bits, v_bits) -> str | None:
-    """'wave' or 'staged': the decode kernel these sizes run on the current device (None: unsupported)."""
+    """'wave', 'wave1' (the wave kernel as one workgroup, no merge kernel) or 'staged': the decode
+    kernel these sizes run on the current device (None: unsupported)."""
     name = _lib.lib().tq_decode_kernel(batch, num_q_heads, num_kv_heads, max_seq_len, k_bits, v_bits)
     return name.decode() if name else None
 

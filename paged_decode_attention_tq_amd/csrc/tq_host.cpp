@@ -544,7 +544,8 @@ const char* tq_decode_kernel(int batch, int num_q_heads, int num_kv_heads, int m
   const int group = num_q_heads / num_kv_heads;
   if (group > tq::kMaxGroup) return nullptr;
   WavePlan wp;
-  if (plan_wave(batch, num_kv_heads, group, max_seq_len, k_bits, v_bits, device_cu_count(), &wp)) return "wave";
+  if (plan_wave(batch, num_kv_heads, group, max_seq_len, k_bits, v_bits, device_cu_count(), &wp))
+    return wp.num_wg == 1 ? "wave1" : "wave";
   SplitPlan p;
   if (plan_split(batch, num_kv_heads, group, max_seq_len, k_bits, v_bits, device_cu_count(), &p)) return "staged";
   return nullptr;

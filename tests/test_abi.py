@@ -88,3 +88,16 @@ def test_status_strings_and_argument_errors():
 def test_context_rejects_other_head_dims():
     with pytest.raises(ValueError):
         api.Context(64, 42)
+
+
+def test_decode_kernel_choice():
+    # host-only planning (no device: the compute-unit count defaults to 256)
+    assert api.decode_kernel(1, 2, 1, 64, 4, 4) == "wave1"          # 4 pages: one workgroup, no merge kernel
+    assert api.decode_kernel(8, 16, 2, 64, 4, 4) == "wave1"         # 32 pages
+    assert api.decode_kernel(3, 16, 2, 200, 4, 4) == "wave"         # 39 pages: split over workgroups
+    assert api.decode_kernel(65, 16, 2, 16, 4, 4) == "wave"         # more than 64 sequences
+    assert api.decode_kernel(32, 16, 2, 2048, 4, 4) == "wave"       # pages geometry
+    assert api.decode_kernel(8, 64, 8, 131072, 4, 4) == "staged"    # 8 KV heads
+    assert api.decode_kernel(2, 16, 1, 64, 4, 4) == "staged"        # 16 query heads per KV head
+    assert api.decode_kernel(2, 16, 3, 64, 4, 4) is None            # 16 % 3 != 0
+    assert api.decode_kernel(2, 8, 2, 64, 7, 4) is None             # 7 bits
