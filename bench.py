@@ -94,6 +94,42 @@ def cpu_baseline(w, kraw, vraw, q, seconds=15.0):
     }
 
 
+def stream_read_ceiling(torch, dev, gib=2, reps=10):
+    """Practical HBM read ceiling on this device: the streaming-read probe
+    (csrc/probe/tq_stream_probe.hip, 16-byte non-temporal loads, 1 KB per wave
+    instruction) over a ``gib`` GiB buffer, timed with events; GB/s (best, mean)."""
+    import ctypes
+
+    path = os.path.join(ROOT, "paged_decode_attention_tq_amd", "libtq_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.tq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p]
+    lib.tq_probe_stream_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    blocks = 2048
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(blocks * 512, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        st = lib.tq_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream)
+        if st != 0:
+            raise RuntimeError(f"stream-read probe launch failed (hip error {st})")
+
+    for _ in range(3):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    del buf, sink
+    return {"kernel": "tq_probe_stream_read (16-byte non-temporal loads)", "bytes": nbytes,
+            "best_gbps": nbytes / (ms.min() / 1e3) / 1e9, "mean_gbps": nbytes / (ms.mean() / 1e3) / 1e9}
+
+
 def traffic_bytes(config):
     """HBM bytes per decode call of this config from the committed counter
     profile, if it was taken on the current decode sources (else None)."""
@@ -117,6 +153,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="long_context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush (1 GiB write, then 1 GiB read) before each timed step")
     args = ap.parse_args()
@@ -146,10 +183,28 @@ def main():
     slots = torch.from_numpy(w.slots).to(dev)
     kraw_d = torch.from_numpy(kraw).to(dev)
     vraw_d = torch.from_numpy(vraw).to(dev)
-    api.write_kv(ctx, kraw_d, kp, slots, w.k_bits)
-    api.write_kv(ctx, vraw_d, vp, slots, w.v_bits)
+    # the prefill (every row of every sequence, K then V), timed as the row
+    # writer's throughput: raw rows read + packed rows written
+    warm_slot = torch.zeros(1, dtype=torch.int64, device=dev)  # first launches of both writers, on a spare page
+    for pages_shape, bits, raw in ((w.page_shape(w.k_bits), w.k_bits, kraw_d), (w.page_shape(w.v_bits), w.v_bits, vraw_d)):
+        spare = torch.zeros((1,) + tuple(pages_shape[1:]), dtype=torch.uint8, device=dev)
+        api.write_kv(ctx, raw[:1].contiguous(), spare, warm_slot, bits)
     torch.cuda.synchronize()
-    log("[bench] pages written (prefill)")
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    wev[0].record()
+    api.write_kv(ctx, kraw_d, kp, slots, w.k_bits)
+    wev[1].record()
+    api.write_kv(ctx, vraw_d, vp, slots, w.v_bits)
+    wev[2].record()
+    torch.cuda.synchronize()
+    write_s = wev[0].elapsed_time(wev[2]) / 1e3
+    kept = int((w.slots >= 0).sum()) * Hkv
+    write_bytes = kraw_d.numel() * kraw_d.element_size() + vraw_d.numel() * vraw_d.element_size() + \
+        kept * (w.row_bytes(w.k_bits) + w.row_bytes(w.v_bits))
+    write = {"rows": 2 * kraw_d.shape[0] * Hkv, "ms": write_s * 1e3, "rows_per_s": 2 * kraw_d.shape[0] * Hkv / write_s,
+             "gbps": write_bytes / write_s / 1e9, "bytes": write_bytes}
+    log(f"[bench] pages written (prefill): {write['rows']} rows in {write['ms']:.3f} ms, "
+        f"{write['rows_per_s'] / 1e6:.1f} M rows/s, {write['gbps']:.0f} GB/s")
 
     # per-step inputs: the last token of every sequence is (re)written each step
     last = torch.from_numpy((w.cu_seqlens[1:] - 1).astype(np.int64)).to(dev)
@@ -245,8 +300,14 @@ def main():
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic_bytes(w.name),
         },
+        "prefill_write": write,
+        "stream_read_ceiling": None,
         "cpu_baseline": None,
     }
+    if not args.no_stream_ceiling:
+        result["stream_read_ceiling"] = stream_read_ceiling(torch, dev)
+        log(f"[bench] streaming-read ceiling: {result['stream_read_ceiling']['best_gbps']:.0f} GB/s best, "
+            f"{result['stream_read_ceiling']['mean_gbps']:.0f} GB/s mean")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(w, kraw, vraw, q, args.cpu_seconds)

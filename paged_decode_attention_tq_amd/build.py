@@ -7,7 +7,10 @@ solver), ``csrc/tq_write.hip`` (row writer), ``csrc/tq_decode.hip`` (staged
 paged decode and merge) and ``csrc/tq_decode_wave.hip`` (wave-private paged
 decode and merge) and ``csrc/tq_scratch.hip`` (the static scratch of the
 allocation-free decode) for gfx950 with hipcc into
-``paged_decode_attention_tq_amd/libtq.so``.
+``paged_decode_attention_tq_amd/libtq.so``, and the measurement probe
+``csrc/probe/tq_stream_probe.hip`` (a streaming-read kernel that bench.py
+times as the practical HBM ceiling; not part of the TQ path) into
+``libtq_probe.so``.
 """
 
 from __future__ import annotations
@@ -22,6 +25,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtq.so")
+PROBE_LIB = os.path.join(PKG, "libtq_probe.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "tq_stream_probe.hip")
 
 # packed fp32 VALU forms are disabled for all device code
 HIP_FLAGS = [
@@ -73,6 +78,11 @@ def build(verbose: bool = False) -> str:
             failed = cmd
     if failed:
         raise RuntimeError(f"build failed: {' '.join(failed)}")
+    probe_tmp = PROBE_LIB + ".tmp"
+    probe = [hipcc(), *HIP_FLAGS, "-shared", PROBE_SRC, "-o", probe_tmp]
+    if verbose:
+        print(" ".join(probe), flush=True)
+    probe_proc = subprocess.Popen(probe, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     link = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(link), flush=True)
@@ -83,6 +93,11 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     for obj in objs:
         os.remove(obj)
+    out, _ = probe_proc.communicate()
+    if probe_proc.returncode != 0:
+        sys.stderr.write(out)
+        raise RuntimeError(f"build failed: {' '.join(probe)}")
+    os.replace(probe_tmp, PROBE_LIB)
     return LIB
 
 
