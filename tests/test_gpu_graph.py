@@ -23,11 +23,13 @@ def ctx():
     return api.Context(128, 42)
 
 
-@pytest.mark.parametrize("hkv,G", [(2, 8), (8, 8)])  # wave-private and staged decode kernels
-def test_graph_replays_equal_eager(ctx, hkv, G):
-    w = workloads.make_workload(f"graph{hkv}", num_q_heads=hkv * G, num_kv_heads=hkv, seq_lens=[700, 33, 1500],
-                                seed=40 + hkv)
-    print(f"[graph] Hkv={hkv} G={G} lens={w.seq_lens.tolist()}", flush=True)
+# wave-private (with its merge kernel), wave-private as one workgroup (no
+# merge kernel), staged
+@pytest.mark.parametrize("hkv,G,lens", [(2, 8, [700, 33, 1500]), (1, 2, [64, 17, 0]), (8, 8, [700, 33, 1500])])
+def test_graph_replays_equal_eager(ctx, hkv, G, lens):
+    w = workloads.make_workload(f"graph{hkv}", num_q_heads=hkv * G, num_kv_heads=hkv, seq_lens=lens, seed=40 + hkv)
+    kernel = api.decode_kernel(w.batch, w.num_q_heads, hkv, w.max_seq_len, 4, 4)
+    print(f"[graph] Hkv={hkv} G={G} lens={w.seq_lens.tolist()} kernel={kernel}", flush=True)
     dev = torch.device("cuda")
     kp = torch.zeros(w.page_shape(4), dtype=torch.uint8, device=dev)
     vp = torch.zeros(w.page_shape(4), dtype=torch.uint8, device=dev)
@@ -35,8 +37,8 @@ def test_graph_replays_equal_eager(ctx, hkv, G):
     kraw = torch.from_numpy(w.rows("k")).to(dev)
     vraw = torch.from_numpy(w.rows("v")).to(dev)
     api.write_kv_pair(ctx, kraw, vraw, kp, vp, slots, 4, 4)
-    # the step: rewrite the last token of every sequence, then decode
-    last = torch.from_numpy((w.cu_seqlens[1:] - 1).astype(np.int64)).to(dev)
+    # the step: rewrite the last token of every non-empty sequence, then decode
+    last = torch.from_numpy((w.cu_seqlens[1:] - 1)[w.seq_lens > 0].astype(np.int64)).to(dev)
     new_slots = slots[last].contiguous()
     k_new, v_new = kraw[last].contiguous(), vraw[last].contiguous()
     q = torch.from_numpy(w.queries()).to(dev)
