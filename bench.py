@@ -84,6 +84,7 @@ def cpu_baseline(w, kraw, vraw, q, seconds=15.0):
         "value": w.batch / t_step,
         "unit": "decode tokens/s",
         "packed_kv_gbps": w.packed_kv_bytes() / t_step / 1e9,
+        "write_rows_per_s": 2 * Ls * w.num_kv_heads / t_write,
         "cores": blas_threads if blas_threads else cores,
         "host_cores": cores,
         "kind": "oracle",
