@@ -728,27 +728,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
   float y0 = 0.0f, y1 = 0.0f;
-  int sidx = 0;
-  // 16 splits per round: all their loads are in flight together
-  constexpr int kU = 16;
-  for (; sidx + kU <= ns; sidx += kU) {
+  // rounds of 8 splits with all their loads in flight together (a split past
+  // the end is not read)
+  constexpr int kU = 8;
+  for (int sidx = 0; sidx < ns; sidx += kU) {
     float v0[kU], v1[kU], wu[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      v0[u] = pa[(int64_t)(sidx + u) * kHeadDim + lane];
-      v1[u] = pa[(int64_t)(sidx + u) * kHeadDim + lane + 64];
-      wu[u] = __shfl(wgt, sidx + u);
+      const bool in = sidx + u < ns;
+      wu[u] = in ? __shfl(wgt, min(sidx + u, 63)) : 0.0f;
+      v0[u] = in ? pa[(int64_t)(sidx + u) * kHeadDim + lane] : 0.0f;
+      v1[u] = in ? pa[(int64_t)(sidx + u) * kHeadDim + lane + 64] : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       y0 += wu[u] * v0[u];
       y1 += wu[u] * v1[u];
     }
-  }
-  for (; sidx < ns; ++sidx) {
-    const float wv = __shfl(wgt, sidx);
-    y0 += wv * pa[(int64_t)sidx * kHeadDim + lane];
-    y1 += wv * pa[(int64_t)sidx * kHeadDim + lane + 64];
   }
   const float inv = 1.0f / den;
   y0 *= inv;

@@ -134,6 +134,24 @@ def test_zero_and_single_token_sequences(ctx):
     assert not out[0].any() and not out[2].any()
 
 
+@pytest.mark.parametrize("B,hkv,G", [(3, 2, 8), (70, 1, 4), (5, 8, 8)])
+def test_all_sequences_empty(ctx, B, hkv, G):
+    # every length 0: the output is all zeros, written over whatever out held
+    # (one-workgroup wave decode, a batch past its 64-sequence bound, staged)
+    dev = torch.device("cuda")
+    rb = 68
+    kp = torch.zeros((2, 16, hkv, rb), dtype=torch.uint8, device=dev)
+    vp = torch.zeros_like(kp)
+    q = torch.randn((B, hkv * G, 128), dtype=torch.float16, device=dev)
+    bt = torch.zeros((B, 1), dtype=torch.int32, device=dev)
+    lens = torch.zeros(B, dtype=torch.int32, device=dev)
+    out = torch.full((B, hkv * G, 128), float("nan"), dtype=torch.float32, device=dev)
+    print(f"[empty] B={B} Hkv={hkv} G={G} kernel={api.decode_kernel(B, hkv * G, hkv, 0, 4, 4)}", flush=True)
+    api.paged_decode(ctx, q, kp, vp, bt, lens, 4, 4, max_seq_len=0, out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
 def test_large_and_small_norms(ctx):
     # values far from unit scale: weights must neither overflow nor lose precision
     for sigma, scale_raw, q_mul in ((3.0, 1.0, 1.0), (0.5, 3e3, 1 / 3e3), (0.5, 1e-3, 1.0), (1.0, 1.0, 40.0),
