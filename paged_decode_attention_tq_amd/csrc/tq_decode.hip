@@ -728,17 +728,18 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off);
   float y0 = 0.0f, y1 = 0.0f;
-  // rounds of 8 splits with all their loads in flight together (a split past
-  // the end is not read)
-  constexpr int kU = 8;
+  // rounds of 16 splits with all their loads in flight together; past the
+  // end a round reads the last split again (every split below ns wrote its
+  // partial) with weight 0, so the loads need no branches
+  constexpr int kU = 16;
   for (int sidx = 0; sidx < ns; sidx += kU) {
     float v0[kU], v1[kU], wu[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const bool in = sidx + u < ns;
-      wu[u] = in ? __shfl(wgt, min(sidx + u, 63)) : 0.0f;
-      v0[u] = in ? pa[(int64_t)(sidx + u) * kHeadDim + lane] : 0.0f;
-      v1[u] = in ? pa[(int64_t)(sidx + u) * kHeadDim + lane + 64] : 0.0f;
+      const int si = min(sidx + u, ns - 1);
+      wu[u] = sidx + u < ns ? __shfl(wgt, si) : 0.0f;
+      v0[u] = pa[(int64_t)si * kHeadDim + lane];
+      v1[u] = pa[(int64_t)si * kHeadDim + lane + 64];
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
