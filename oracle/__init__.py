@@ -40,6 +40,7 @@ from .codec import (
     bytes_to_rows,
     dequantize_rows,
     write_kv,
+    decompress_kv,
     OracleCodec,
 )
 from .attention import paged_decode, paged_decode_heads
@@ -62,6 +63,7 @@ __all__ = [
     "bytes_to_rows",
     "dequantize_rows",
     "write_kv",
+    "decompress_kv",
     "OracleCodec",
     "paged_decode",
     "paged_decode_heads",

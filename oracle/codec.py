@@ -48,6 +48,7 @@ __all__ = [
     "bytes_to_rows",
     "dequantize_rows",
     "write_kv",
+    "decompress_kv",
     "OracleCodec",
     "NEAR_BOUNDARY",
 ]
@@ -179,6 +180,35 @@ def write_kv(raw, pages, slots, bits: int, signs, t64):
     return out, near_all
 
 
+def decompress_kv(pages, slots, bits: int, signs, c32):
+    """Dense rows read back from ``pages[NB, BS, Hkv, RB]`` -> float64 ``[N, Hkv, d]``.
+
+    Sources: "Architecture", "Data Flow" (packed bytes lead to a diagnostic
+    dense reconstruction, kept apart from compressed attention) and "vLLM
+    Reference Audit", File Map row "TQ4 unpack kernel" (packed index bytes
+    and norms in, rows out, a diagnostic readback into a caller's buffer).
+
+    Token n's row for head h is the row stored at flat slot ``slots[n]``
+    ("vLLM Usage", "Slot Mapping"), reconstructed as ``n * irht(c[idx])``.
+    Readings: a negative slot names no stored row, so its rows are zeros; a
+    slot at or past ``NB * BS`` raises ``IndexError``, as the write does.
+    """
+    pages = np.asarray(pages, dtype=np.uint8)
+    slots = np.asarray(slots, dtype=np.int64)
+    NB, BS, Hkv, RB = pages.shape
+    d = len(signs)
+    if RB != row_bytes(d, bits) or slots.ndim != 1:
+        raise ValueError("shape mismatch")
+    if np.any(slots >= NB * BS):
+        raise IndexError("slot outside the allocated pages")
+    out = np.zeros((slots.shape[0], Hkv, d), dtype=np.float64)
+    keep = slots >= 0
+    if np.any(keep):
+        s = slots[keep]
+        out[keep] = dequantize_rows(pages[s // BS, s % BS], bits, d, signs, c32)
+    return out
+
+
 class OracleCodec:
     """Signs and codebooks for one head_dim and rotation seed."""
 
@@ -208,6 +238,9 @@ class OracleCodec:
 
     def write_kv(self, raw, pages, slots, bits):
         return write_kv(raw, pages, slots, bits, self.signs, self.boundaries(bits))
+
+    def decompress_kv(self, pages, slots, bits):
+        return decompress_kv(pages, slots, bits, self.signs, self.centroids32(bits))
 
 
 def norm_bytes(norm32) -> bytes:
