@@ -147,6 +147,96 @@ def traffic_bytes(config):
     return prof.get("configs", {}).get(config, {}).get("bytes_per_call")
 
 
+def cpu_decompress_baseline(w, kp_host, seconds=15.0):
+    """Time the oracle's readback (``oracle.decompress_kv``) on a bounded
+    sample: blocks of 2048 tokens (all KV heads) of the workload's slots,
+    repeated until about ``seconds`` have been spent; rows/s."""
+    import oracle
+
+    codec = oracle.OracleCodec(w.head_dim, w.rht_seed)
+    rows, t0 = 0, time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        s = w.slots[i * 2048:(i + 1) * 2048]
+        codec.decompress_kv(kp_host, s, w.k_bits)
+        rows += len(s) * w.num_kv_heads
+        i += 1
+    el = time.perf_counter() - t0
+    return {"value": rows / el, "unit": "rows/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{i} blocks of 2048 tokens x {w.num_kv_heads} KV heads of the workload's K pages, {el:.1f} s"}
+
+
+def bench_decompress(args, torch, api, w, ctx, kp, slots):
+    """Dense readback of every K row of the workload (one tq_decompress_kv call
+    over all tokens), timed with events on the library's stream."""
+    dt = {"fp16": torch.float16, "bf16": torch.bfloat16, "fp32": torch.float32}[args.out_dtype]
+    dev = kp.device
+    N, Hkv, d = w.num_tokens, w.num_kv_heads, w.head_dim
+    out = torch.empty((N, Hkv, d), dtype=dt, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_rd = None if args.no_flush else torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def call(i=None):
+        if flush is not None:
+            flush.zero_()
+            flush_rd.sum()
+        if i is not None:
+            ev[i][0].record()
+        api.decompress_kv(ctx, kp, slots, w.k_bits, out=out, err_count=err, check_slots=False)
+        if i is not None:
+            ev[i][1].record()
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    rows = N * Hkv
+    kept = int((w.slots >= 0).sum()) * Hkv
+    nbytes = 8 * N + kept * w.row_bytes(w.k_bits) + rows * d * out.element_size()
+    sec = float(ms.mean()) / 1e3
+    log(f"[bench] decompress ms per call: mean {ms.mean():.4f} median {np.median(ms):.4f} min {ms.min():.4f}")
+    result = {
+        "metric": "TQ dense readback rows/s + HBM GB/s (% of peak), 1 MI355X",
+        "value": rows / sec,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": float(ms.mean()),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"u8 packed K{w.k_bits} rows in, fp32 reconstruction, {args.out_dtype} rows out",
+        "data": "synthetic (the workload's K rows written by the row writer)",
+        "config": {"workload": f"{w.name} K pages: {N} tokens x Hkv {Hkv}, head_dim {d}, block 16, K{w.k_bits}, "
+                               f"{args.out_dtype} out", "rows": rows},
+        "decompress_ms": float(ms.mean()),
+        "decompress_ms_median": float(np.median(ms)),
+        "decompress_ms_min": float(ms.min()),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "tq_decompress_kv (decompress_rows_kernel)",
+            "achieved": nbytes / sec / 1e9,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": nbytes / sec / 1e9 / HBM_PEAK_GBPS,
+            "algorithmic_bytes": nbytes,
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle readback on the host")
+        result["cpu_baseline"] = cpu_decompress_baseline(w, kp.cpu().numpy(), min(args.cpu_seconds, 15.0))
+    return result
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +247,10 @@ def main():
     ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush (1 GiB write, then 1 GiB read) before each timed step")
+    ap.add_argument("--op", choices=("decode", "decompress"), default="decode",
+                    help="decode: the decode step (default); decompress: the dense readback of every K row")
+    ap.add_argument("--out-dtype", choices=("fp16", "bf16", "fp32"), default="fp16",
+                    help="output dtype of the dense readback (--op decompress)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -206,6 +300,11 @@ def main():
              "gbps": write_bytes / write_s / 1e9, "bytes": write_bytes}
     log(f"[bench] pages written (prefill): {write['rows']} rows in {write['ms']:.3f} ms, "
         f"{write['rows_per_s'] / 1e6:.1f} M rows/s, {write['gbps']:.0f} GB/s")
+
+    if args.op == "decompress":
+        del kraw_d, vraw_d
+        print(json.dumps(bench_decompress(args, torch, api, w, ctx, kp, slots)), flush=True)
+        return
 
     # per-step inputs: the last token of every sequence is (re)written each step
     last = torch.from_numpy((w.cu_seqlens[1:] - 1).astype(np.int64)).to(dev)

@@ -2,8 +2,9 @@
  * tq.h -- C ABI of the TurboQuant packed-page KV library for AMD Instinct
  * MI355X (gfx950).
  *
- * The library writes K/V rows into uint8 pages in the TQ row format and runs
- * single-query paged decode attention over those pages.  Everything below is
+ * The library writes K/V rows into uint8 pages in the TQ row format, reads
+ * them back as dense rows, and runs single-query paged decode attention over
+ * those pages.  Everything below is
  * plain C: device buffers are raw device pointers, streams are hipStream_t
  * passed as void*.  The library never allocates device memory inside
  * tq_write_kv / tq_paged_decode and never synchronises the stream; the caller
@@ -136,6 +137,31 @@ tq_status tq_write_kv_pair(const tq_ctx* ctx, const void* raw_k, const void* raw
                            uint8_t* k_pages, int k_bits, uint8_t* v_pages, int v_bits,
                            int64_t num_blocks, int block_size, const int64_t* slots,
                            int32_t* err_count, void* stream);
+
+/* Dense readback of stored rows: the diagnostic reconstruction of packed
+ * bytes ("Architecture", section "Data Flow"; "vLLM Reference Audit", File
+ * Map row "TQ4 unpack kernel": packed index bytes and norms in, rows out,
+ * into a caller-given buffer).  The row of token n and KV head h is the TQ
+ * row at flat slot slots[n] ("vLLM Usage", "Slot Mapping"), reconstructed
+ * as x = n * s * (H c[idx]) / sqrt(head_dim): the fp32 centroids of its
+ * indices, the inverse rotation, the stored norm.
+ *   pages      device, uint8 [num_blocks, block_size, num_kv_heads,
+ *              tq_row_bytes(head_dim, bits)], contiguous, 4-byte aligned.
+ *   bits       2..5.
+ *   slots      device, int64 [num_tokens], 8-byte aligned.  slot < 0: the
+ *              token's rows are written as zeros.  slot >= num_blocks *
+ *              block_size: zeros too, and counted in *err_count.
+ *   out        device, [num_tokens, num_kv_heads, head_dim] of out_dtype
+ *              (fp32, fp16 or bf16, rounded to nearest even), contiguous,
+ *              16-byte aligned; every element is written.
+ *   err_count  device int32 or NULL; the kernel atomically ADDS the number of
+ *              out-of-range slots (the caller zeroes it beforehand).
+ * num_tokens * num_kv_heads must stay below 2^31 (TQ_ERR_UNSUPPORTED).
+ * Asynchronous, allocates nothing; TQ_ERR_NO_DEVICE when the current device
+ * is not a gfx950. */
+tq_status tq_decompress_kv(const tq_ctx* ctx, const uint8_t* pages, int64_t num_blocks, int block_size,
+                           int num_kv_heads, int bits, const int64_t* slots, int64_t num_tokens,
+                           void* out, tq_dtype out_dtype, int32_t* err_count, void* stream);
 
 /* Bytes of device workspace tq_paged_decode needs for these sizes (the
  * split partials: a normalised rotated sum and a log-sum-exp per query head

@@ -44,6 +44,11 @@ SIGNATURES = {
         [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int,
          _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p],
     ),
+    "tq_decompress_kv": (
+        _c.c_int,
+        [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_int64,
+         _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p],
+    ),
     "tq_decode_kernel": (_c.c_char_p, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
     "tq_decode_workspace_bytes": (
         _c.c_size_t, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),

@@ -1,7 +1,7 @@
 """Python entry points over the C ABI (same names as include/tq.h).
 
 PyTorch supplies device memory and the current HIP stream; every step of
-the write and the decode runs in the HIP kernels of ``libtq.so``.
+the write, the readback and the decode runs in the HIP kernels of ``libtq.so``.
 """
 
 from __future__ import annotations
@@ -22,6 +22,7 @@ __all__ = [
     "Context",
     "write_kv",
     "write_kv_pair",
+    "decompress_kv",
     "decode_workspace_bytes",
     "decode_kernel",
     "paged_decode",
@@ -147,6 +148,39 @@ def write_kv_pair(ctx: Context, raw_k: torch.Tensor, raw_v: torch.Tensor, k_page
             raise TQError(f"tq_write_kv_pair: {n_bad} slot(s) outside the allocated pages")
         return n_bad
     return 0
+
+
+def decompress_kv(ctx: Context, pages: torch.Tensor, slots: torch.Tensor, bits: int,
+                  out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                  err_count: torch.Tensor | None = None, check_slots: bool = True) -> torch.Tensor:
+    """Dense rows ``[N, Hkv, d]`` read back from ``pages[NB, BS, Hkv, RB]`` at ``slots[N]``.
+
+    Negative slots give zero rows.  Out-of-range slots give zero rows and are
+    counted; with ``check_slots`` the call synchronises and raises
+    ``TQError`` if any were found.
+    """
+    _need(pages.is_cuda and slots.is_cuda, "tensors must be on the GPU")
+    _need(pages.dtype == torch.uint8 and pages.dim() == 4 and pages.is_contiguous(), "pages must be uint8 4-D")
+    NB, BS, Hkv, RB = pages.shape
+    _need(RB == row_bytes(ctx.head_dim, bits), "pages row_bytes does not match bits")
+    _need(slots.dtype == torch.int64 and slots.dim() == 1 and slots.is_contiguous(), "slots must be int64 [N]")
+    N = slots.shape[0]
+    if out is None:
+        out = torch.empty((N, Hkv, ctx.head_dim), dtype=out_dtype, device=pages.device)
+    _need(out.dtype in _DTYPES and out.shape == (N, Hkv, ctx.head_dim) and out.is_contiguous(),
+          "out must be fp32/fp16/bf16 [N, Hkv, d]")
+    own = err_count is None and check_slots
+    if own:
+        err_count = torch.zeros(1, dtype=torch.int32, device=pages.device)
+    st = _lib.lib().tq_decompress_kv(
+        ctx.handle, pages.data_ptr(), NB, BS, Hkv, bits, slots.data_ptr(), N, out.data_ptr(), _DTYPES[out.dtype],
+        err_count.data_ptr() if err_count is not None else None, _stream(pages))
+    check(st, "tq_decompress_kv")
+    if check_slots:
+        n_bad = int(err_count.item())
+        if n_bad:
+            raise TQError(f"tq_decompress_kv: {n_bad} slot(s) outside the allocated pages")
+    return out
 
 
 def decode_workspace_bytes(ctx: Context, batch, num_q_heads, num_kv_heads, max_seq_len, block_size=16) -> int:

@@ -30,16 +30,6 @@ struct PairTable {
   static constexpr int kBytes = kRows * kStride;
 };
 
-// Centroid (lane & 31) of a kernel-argument table of 2^B entries (scalar
-// loads, as in pick4); the table fills gather from it with lane shuffles.
-template <int B>
-__device__ __forceinline__ float cent_of_lane(const float* cent, int lane) {
-  float v = 0.0f;
-#pragma unroll
-  for (int j = 0; j < (1 << B); ++j) v = ((lane & 31) == j) ? cent[j] : v;
-  return v;
-}
-
 template <int B>
 __device__ __forceinline__ void fill_pair_table(uint8_t* base, const float* cent, int tid, int nthreads) {
   using T = PairTable<B>;

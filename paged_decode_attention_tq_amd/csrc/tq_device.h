@@ -64,6 +64,16 @@ __device__ __forceinline__ uint32_t pick4(const uint32_t* w, int idx) {
   return (idx & 2) ? ((idx & 1) ? w3 : w2) : ((idx & 1) ? w1 : w0);
 }
 
+// Centroid (lane & 31) of a kernel-argument table of 2^B entries (scalar
+// loads, as in pick4); lookups gather from it with lane shuffles.
+template <int B>
+__device__ __forceinline__ float cent_of_lane(const float* cent, int lane) {
+  float v = 0.0f;
+#pragma unroll
+  for (int j = 0; j < (1 << B); ++j) v = ((lane & 31) == j) ? cent[j] : v;
+  return v;
+}
+
 __device__ __forceinline__ uint32_t pack_half2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }

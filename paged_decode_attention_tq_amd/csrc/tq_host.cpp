@@ -514,6 +514,44 @@ tq_status tq_write_kv_pair(const tq_ctx* ctx, const void* raw_k, const void* raw
   return hip_status(tq::launch_write_pair(k, v, (int)raw_dtype, k_bits, v_bits, (hipStream_t)stream));
 }
 
+tq_status tq_decompress_kv(const tq_ctx* ctx, const uint8_t* pages, int64_t num_blocks, int block_size,
+                           int num_kv_heads, int bits, const int64_t* slots, int64_t num_tokens, void* out,
+                           tq_dtype out_dtype, int32_t* err_count, void* stream) {
+  if (!ctx || num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || block_size <= 0)
+    return TQ_ERR_INVALID_ARG;
+  if (out_dtype != TQ_F32 && out_dtype != TQ_F16 && out_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!bits_ok(bits)) return TQ_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return TQ_OK;  // nothing to read (pointers unused)
+  if (!pages || !slots || !out) return TQ_ERR_INVALID_ARG;
+  if (num_tokens > (INT64_C(1) << 31) / num_kv_heads - 1) return TQ_ERR_UNSUPPORTED;  // rows < 2^31
+  if ((reinterpret_cast<uintptr_t>(pages) & 3) || (reinterpret_cast<uintptr_t>(slots) & 7) ||
+      (reinterpret_cast<uintptr_t>(out) & 15))
+    return TQ_ERR_ALIGNMENT;
+  tq::ReadArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.pages = pages;
+  a.slots = slots;
+  a.out = out;
+  a.err_count = err_count;
+  a.num_rows = (uint32_t)(num_tokens * num_kv_heads);
+  a.num_slots = num_blocks * block_size;
+  a.row_bytes = (int)tq_row_bytes(kHeadDim, bits);
+  a.page_bytes = (int64_t)block_size * num_kv_heads * a.row_bytes;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  if (a.page_bytes >= (INT64_C(1) << 31)) return TQ_ERR_UNSUPPORTED;
+  a.hkv_shift = (num_kv_heads & (num_kv_heads - 1)) ? -1 : __builtin_ctz((unsigned)num_kv_heads);
+  a.bs_shift = (block_size & (block_size - 1)) ? -1 : __builtin_ctz((unsigned)block_size);
+  std::memcpy(a.cent, ctx->cent[bits], sizeof(float) << bits);
+  for (int q = 0; q < 4; ++q) {
+    const bool odd = ((q ^ (q >> 1)) & 1) != 0;  // popcount(q) odd
+    for (int j = 0; j < 32; ++j)
+      if ((ctx->signs[32 * q + j] < 0) != odd) a.neg_bits[q] |= 1u << j;
+  }
+  if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
+  return hip_status(tq::launch_decompress(a, bits, (int)out_dtype, device_cu_count(), (hipStream_t)stream));
+}
+
 size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads, int num_kv_heads,
                                  int max_seq_len, int block_size) {
   (void)ctx;

@@ -1,5 +1,5 @@
 // Internal structures shared by the host code (tq_host.cpp) and the HIP
-// kernels (tq_write.hip, tq_decode.hip).  Not part of the public ABI.
+// kernels (tq_write.hip, tq_decompress.hip, tq_decode.hip, tq_decode_wave.hip).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,6 +26,27 @@ struct WriteArgs {
   int32_t row_bytes;
   uint32_t sign_bits[kHeadDim / 32];   // bit i set <=> sign_i = -1
   float pos_bounds[16];     // the 2^(b-1) - 1 positive boundaries, increasing
+};
+
+// Arguments of the dense readback kernel (tq_decompress.hip).
+struct ReadArgs {
+  const uint8_t* pages;     // [num_blocks, block_size, num_kv_heads, row_bytes]
+  const int64_t* slots;     // [num_tokens]
+  void* out;                // [num_tokens, num_kv_heads, 128] of the output dtype, 16-byte aligned
+  int32_t* err_count;       // nullable
+  int64_t num_slots;        // num_blocks * block_size
+  int64_t page_bytes;       // block_size * num_kv_heads * row_bytes (< 2^31)
+  uint32_t num_rows;        // num_tokens * num_kv_heads (< 2^31)
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t row_bytes;
+  int32_t hkv_shift;        // log2(num_kv_heads), or -1 when not a power of two
+  int32_t bs_shift;         // log2(block_size), or -1 when not a power of two
+  float cent[32];           // the 2^bits fp32 centroids
+  // Sign of coordinate 32 q + j as held by quad lane q: bit j of neg_bits[q]
+  // is set when the rotation sign s_(32q+j) times the parity sign
+  // (-1)^popcount(q) that the quad butterflies leave is negative.
+  uint32_t neg_bits[4];
 };
 
 // Arguments of the decode split kernel.  One workgroup handles one
@@ -152,6 +173,7 @@ hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t
 // K and V rows of the same tokens (same num_rows) in one launch
 hipError_t launch_write_pair(const WriteArgs& k, const WriteArgs& v, int raw_dtype, int k_bits, int v_bits,
                              hipStream_t stream);
+hipError_t launch_decompress(const ReadArgs& a, int bits, int out_dtype, int num_cus, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, hipStream_t stream);
 int decode_table_bytes(int k_bits, int v_bits);  // LDS bytes of the decode lookup tables
 int decode_merge_lds_bytes();                     // LDS bytes of the stream merge

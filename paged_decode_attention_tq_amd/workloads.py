@@ -26,7 +26,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-__all__ = ["Workload", "make_workload", "PRESETS", "preset"]
+__all__ = ["Workload", "make_workload", "PRESETS", "preset", "random_pages"]
 
 
 def _rng(seed, *key):
@@ -229,3 +229,18 @@ def preset(name: str, **overrides) -> Workload:
     kw = dict(PRESETS[name])
     kw.update(overrides)
     return make_workload(name, **kw)
+
+
+def random_pages(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, bits: int,
+                 seed: int = 0) -> np.ndarray:
+    """Page bytes ``uint8 [NB, BS, Hkv, RB]`` whose rows hold uniform random
+    index bytes and a random positive float32 norm (last four bytes,
+    little-endian), from the stream ``(4,)`` of ``seed``.  No row is encoded:
+    these are inputs for readers of pages, not outputs of a writer."""
+    ib = (head_dim * bits + 7) // 8
+    g = _rng(seed, 4)
+    shape = (num_blocks, block_size, num_kv_heads)
+    idx = g.integers(0, 256, size=shape + (ib,), dtype=np.uint8)
+    norm = (math.sqrt(head_dim) * g.lognormal(0.0, 0.5, size=shape)).astype("<f4")
+    return np.concatenate([idx, norm[..., None].view(np.uint8)], axis=-1)
+

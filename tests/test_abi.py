@@ -69,6 +69,16 @@ def test_status_strings_and_argument_errors():
     assert pw(h, None, None, 1, 0, 2, None, 4, None, 2, 4, 16, None, None, None) == 0  # nothing to do
     assert pw(h, ctypes.c_void_p(64), ctypes.c_void_p(66), 1, 4, 2, ctypes.c_void_p(64), 4,
               ctypes.c_void_p(64), 4, 4, 16, ctypes.c_void_p(64), None, None) == 3  # raw_v misaligned
+    # the dense readback
+    rd = lib.tq_decompress_kv
+    assert rd(h, a64, 4, 16, 2, 6, a64, 5, a64, 0, None, None) == 2  # bits 6
+    assert rd(h, a64, 4, 16, 2, 4, a64, 5, a64, 7, None, None) == 1  # bad out dtype
+    assert rd(h, None, 4, 16, 2, 4, a64, 5, a64, 0, None, None) == 1  # null pages
+    assert rd(h, a64, 4, 16, 0, 4, a64, 5, a64, 0, None, None) == 1  # no KV heads
+    assert rd(h, a64, 4, 16, 2, 4, a64, 0, None, 0, None, None) == 0  # nothing to read
+    assert rd(h, a64, 4, 16, 2, 4, ctypes.c_void_p(68), 5, a64, 0, None, None) == 3  # slots not 8-byte aligned
+    assert rd(h, a64, 4, 16, 2, 4, a64, 5, ctypes.c_void_p(72), 0, None, None) == 3  # out not 16-byte aligned
+    assert rd(h, a64, 4, 16, 2, 4, a64, 1 << 30, a64, 0, None, None) == 2  # 2^31 rows
     p = ctypes.c_void_p(16)
     args = dict(batch=2, hq=128, hkv=1)  # group 128 > 64
     assert lib.tq_paged_decode(h, p, 1, 2, 128, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 2
