@@ -43,7 +43,7 @@ from .codec import (
     decompress_kv,
     OracleCodec,
 )
-from .attention import paged_decode, paged_decode_heads
+from .attention import paged_decode, paged_decode_heads, paged_decode_hybrid
 
 __all__ = [
     "beta_codebook",
@@ -67,4 +67,5 @@ __all__ = [
     "OracleCodec",
     "paged_decode",
     "paged_decode_heads",
+    "paged_decode_hybrid",
 ]

@@ -26,7 +26,7 @@ import numpy as np
 
 from .codec import dequantize_rows
 
-__all__ = ["gather_rows", "paged_decode", "paged_decode_heads"]
+__all__ = ["gather_rows", "paged_decode", "paged_decode_heads", "paged_decode_hybrid"]
 
 
 def gather_rows(pages, block_table_row, length, kv_head):
@@ -83,3 +83,50 @@ def paged_decode(q, k_pages, v_pages, block_table, seq_lens, k_bits, v_bits,
     out = paged_decode_heads(q, k_pages, v_pages, block_table, seq_lens, k_bits, v_bits,
                              signs, ck32, cv32, heads, scale)
     return out.reshape(B, Hq, d).astype(np.float32)
+
+
+def paged_decode_hybrid(q, k_pages, v_pages, block_table, seq_lens, recent_k, recent_v, recent_lens,
+                        k_bits, v_bits, signs, ck32, cv32, scale=None):
+    """Decode over packed history plus an exact recent window -> float32 ``[B, Hq, d]``.
+
+    Sources: "Integration API" (vLLM hooks, the hybrid mode: compressed
+    history plus the exact recent tokens for decode) and "Architecture",
+    "Cache Lifecycle" (decoded tokens are appended to a recent window before
+    they are flushed to packed pages).
+
+    Readings: sequence b's context is its ``seq_lens[b]`` packed tokens
+    (reconstructed as in ``paged_decode``) together with the first
+    ``recent_lens[b]`` rows of ``recent_k[b] / recent_v[b]``
+    (``[cap, Hkv, d]``, used exactly as given: fp16 / bf16 / fp32 values
+    widened to float64); the window holds tokens the pages do not, and
+    attention is over all of them with one softmax; order does not matter.
+    A sequence with no token at all gives zeros.
+    """
+    q = np.asarray(q)
+    B, Hq, d = q.shape
+    Hkv = k_pages.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    rk = np.asarray(recent_k, dtype=np.float64)
+    rv = np.asarray(recent_v, dtype=np.float64)
+    if rk.shape[0] != B or rk.shape[2:] != (Hkv, d) or rv.shape != rk.shape:
+        raise ValueError("recent window shape mismatch")
+    cap = rk.shape[1]
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    for b in range(B):
+        L, R = int(seq_lens[b]), int(recent_lens[b])
+        if not 0 <= R <= cap:
+            raise ValueError("recent length outside the window")
+        if L + R == 0:
+            continue
+        for g in range(Hkv):
+            K = V = np.zeros((0, d))
+            if L > 0:
+                K = dequantize_rows(gather_rows(k_pages, block_table[b], L, g), k_bits, d, signs, ck32)
+                V = dequantize_rows(gather_rows(v_pages, block_table[b], L, g), v_bits, d, signs, cv32)
+            K = np.concatenate([K, rk[b, :R, g]], axis=0)
+            V = np.concatenate([V, rv[b, :R, g]], axis=0)
+            for h in range(g * G, (g + 1) * G):
+                out[b, h] = _attend(q[b, h].astype(np.float64), K, V, scale)
+    return out.astype(np.float32)
+

@@ -119,6 +119,28 @@ class Workload:
     def zero_pages(self, bits) -> np.ndarray:
         return np.zeros(self.page_shape(bits), dtype=np.uint8)
 
+    def recent_window(self, cap: int, recent_lens, seed: int = 0):
+        """Dense recent-window rows ``(k, v)``, each ``[B, cap, Hkv, d]`` in the
+        workload's dtype, drawn like its K/V rows (N(0,1), the per-token
+        LogNormal scale, the outlier channels) from the streams ``(5, b)`` /
+        ``(6, b)`` of ``seed``; rows past ``recent_lens[b]`` are drawn too (a
+        reader must ignore them)."""
+        lens = np.asarray(recent_lens)
+        if lens.shape != (self.batch,) or np.any(lens < 0) or np.any(lens > cap):
+            raise ValueError("recent_lens must be [B] in 0..cap")
+        out = []
+        for key in (5, 6):
+            x = np.empty((self.batch, cap, self.num_kv_heads, self.head_dim), dtype=np.float32)
+            for b in range(self.batch):
+                rng = _rng(seed, key, b)
+                x[b] = rng.standard_normal((cap, self.num_kv_heads, self.head_dim), dtype=np.float32)
+                if self.lognormal_sigma is not None:
+                    x[b] *= rng.lognormal(0.0, self.lognormal_sigma, size=cap).astype(np.float32)[:, None, None]
+            if self.outliers is not None and len(self.outliers):
+                x[:, :, self.outliers[:, 0], self.outliers[:, 1]] *= np.float32(self.outlier_scale)
+            out.append(x.astype(self.dtype))
+        return out[0], out[1]
+
 
 def make_workload(
     name,
