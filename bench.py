@@ -247,8 +247,10 @@ def main():
     ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush (1 GiB write, then 1 GiB read) before each timed step")
-    ap.add_argument("--op", choices=("decode", "decompress"), default="decode",
-                    help="decode: the decode step (default); decompress: the dense readback of every K row")
+    ap.add_argument("--op", choices=("decode", "decompress", "hybrid"), default="decode",
+                    help="decode: the decode step (default); decompress: the dense readback of every K row; "
+                         "hybrid: the decode step over the packed pages plus an exact fp16 window per sequence")
+    ap.add_argument("--window", type=int, default=128, help="recent-window rows per sequence (--op hybrid)")
     ap.add_argument("--out-dtype", choices=("fp16", "bf16", "fp32"), default="fp16",
                     help="output dtype of the dense readback (--op decompress)")
     args = ap.parse_args()
@@ -315,7 +317,16 @@ def main():
     bt = torch.from_numpy(w.block_table).to(dev)
     lens = torch.from_numpy(w.seq_lens).to(dev)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(api.decode_workspace_bytes(ctx, B, Hq, Hkv, w.max_seq_len), dtype=torch.uint8, device=dev)
+    hybrid = args.op == "hybrid"
+    if hybrid:
+        # a full window of exact rows per sequence, fp16, drawn like the workload's rows
+        rl = np.full(B, args.window, dtype=np.int32)
+        rk, rv = w.recent_window(args.window, rl, seed=1)
+        rk_d, rv_d = torch.from_numpy(rk).to(dev), torch.from_numpy(rv).to(dev)
+        rl_d = torch.from_numpy(rl).to(dev)
+        ws = torch.empty(api.hybrid_workspace_bytes(ctx, B, Hq, Hkv, w.max_seq_len), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(api.decode_workspace_bytes(ctx, B, Hq, Hkv, w.max_seq_len), dtype=torch.uint8, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     del kraw_d, vraw_d
 
@@ -338,8 +349,12 @@ def main():
         api.write_kv_pair(ctx, k_new, v_new, kp, vp, new_slots, w.k_bits, w.v_bits, err_count=err, check_slots=False)
         if i is not None:
             ev[i][1].record()
-        api.paged_decode(ctx, q_d, kp, vp, bt, lens, w.k_bits, w.v_bits, max_seq_len=w.max_seq_len,
-                         out=out, workspace=ws)
+        if hybrid:
+            api.paged_decode_hybrid(ctx, q_d, kp, vp, bt, lens, rk_d, rv_d, rl_d, w.k_bits, w.v_bits,
+                                    max_seq_len=w.max_seq_len, out=out, workspace=ws)
+        else:
+            api.paged_decode(ctx, q_d, kp, vp, bt, lens, w.k_bits, w.v_bits, max_seq_len=w.max_seq_len,
+                             out=out, workspace=ws)
         if i is not None:
             ev[i][2].record()
 
@@ -360,10 +375,16 @@ def main():
     log(f"[bench] step (write + decode) ms: mean {ms_step:.4f}; wall per step incl. cache flush "
         f"{elapsed * 1e3 / args.steps:.4f}")
     packed = w.packed_kv_bytes()
+    window_bytes = 0
+    if hybrid:  # the window rows read (K and V, fp16) count as algorithmic bytes too
+        window_bytes = 2 * B * args.window * Hkv * d * 2
+        packed += window_bytes
     dec_s = float(dec_ms.mean()) / 1e3
     achieved = packed / dec_s / 1e9
     result = {
-        "metric": "paged TQ decode tokens/s + packed-KV HBM GB/s (% of peak), 1 MI355X",
+        "metric": ("paged TQ decode tokens/s + packed-KV HBM GB/s (% of peak), 1 MI355X" if not hybrid else
+                   f"paged TQ hybrid decode (packed history + {args.window}-row exact fp16 window) tokens/s + "
+                   "HBM GB/s (% of peak), 1 MI355X"),
         "value": B / (ms_step / 1e3),
         "unit": "decode tokens/s",
         "n_gpus": 1,
@@ -378,7 +399,8 @@ def main():
         "data": "synthetic (seeded N(0,1) fp16 K/V/q, random page permutation)",
         "config": {
             "workload": f"{w.name}: batch {B} x {w.max_seq_len} tokens, Hq {Hq}, Hkv {Hkv}, head_dim {d}, "
-                        f"block 16, K{w.k_bits}/V{w.v_bits}",
+                        f"block 16, K{w.k_bits}/V{w.v_bits}" +
+                        (f", plus a {args.window}-row fp16 window per sequence" if hybrid else ""),
             "global_batch": B,
             "seq_len": w.max_seq_len,
             "parallelism": "single GPU",
@@ -392,13 +414,14 @@ def main():
         "context_tokens_per_s": float(w.num_tokens) / dec_s,
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"tq_paged_decode, {kernel} decode kernel + merge kernel" if kernel != "wave1" else
-                       "tq_paged_decode, wave decode kernel as one workgroup (no merge kernel)"),
+            "kernel": ((f"tq_paged_decode, {kernel} decode kernel + merge kernel" if kernel != "wave1" else
+                        "tq_paged_decode, wave decode kernel as one workgroup (no merge kernel)") +
+                       (" + hybrid_window_kernel" if hybrid else "")),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": traffic_bytes(w.name),
+            "traffic": None if hybrid else traffic_bytes(w.name),
         },
         "prefill_write": write,
         "stream_read_ceiling": None,
@@ -408,7 +431,9 @@ def main():
         result["stream_read_ceiling"] = stream_read_ceiling(torch, dev)
         log(f"[bench] streaming-read ceiling: {result['stream_read_ceiling']['best_gbps']:.0f} GB/s best, "
             f"{result['stream_read_ceiling']['mean_gbps']:.0f} GB/s mean")
-    if not args.no_cpu_baseline:
+    if hybrid:
+        result["window_bytes"] = window_bytes
+    if not args.no_cpu_baseline and not hybrid:
         log("[bench] timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(w, kraw, vraw, q, args.cpu_seconds)
     print(json.dumps(result), flush=True)

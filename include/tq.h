@@ -4,7 +4,7 @@
  *
  * The library writes K/V rows into uint8 pages in the TQ row format, reads
  * them back as dense rows, and runs single-query paged decode attention over
- * those pages.  Everything below is
+ * those pages, alone or together with an exact window of recent rows.  Everything below is
  * plain C: device buffers are raw device pointers, streams are hipStream_t
  * passed as void*.  The library never allocates device memory inside
  * tq_write_kv / tq_paged_decode and never synchronises the stream; the caller
@@ -219,6 +219,48 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype,
                           const int32_t* seq_lens, int max_seq_len, float scale,
                           float* out, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* Bytes of device workspace tq_paged_decode_hybrid needs: the decode's
+ * workspace (rounded up to 256 bytes) plus one float per query head for the
+ * packed part's log-sum-exp.  Same arguments, rules and device dependence as
+ * tq_decode_workspace_bytes; 0 where that returns 0. */
+size_t tq_hybrid_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads,
+                                 int num_kv_heads, int max_seq_len, int block_size);
+
+/* Decode over packed history plus an exact recent window ("Integration API",
+ * vLLM hooks, hybrid mode: compressed history plus exact recent tokens for
+ * decode; "Architecture", "Cache Lifecycle": decoded tokens are appended to a
+ * recent window before they are flushed to packed pages).  Sequence b attends
+ * with one softmax over its seq_lens[b] packed tokens (exactly as
+ * tq_paged_decode) and the first recent_lens[b] rows of its window, which
+ * hold tokens the pages do not; the order of the window rows does not
+ * matter.  A sequence with no token at all yields zeros.
+ *   q ... max_seq_len, scale, out: as tq_paged_decode.
+ *   recent_k, recent_v  device, [batch, recent_cap, num_kv_heads, head_dim]
+ *                       of recent_dtype (fp32, fp16 or bf16, used exactly as
+ *                       given), contiguous, 16-byte aligned; rows past a
+ *                       sequence's recent length are never read.  May be NULL
+ *                       when recent_cap is 0 (then this is tq_paged_decode).
+ *   recent_lens         device, int32 [batch]; each entry is clamped to
+ *                       0..recent_cap.
+ *   workspace           device, >= tq_hybrid_workspace_bytes(...) bytes,
+ *                       16-byte aligned; contents are scratch.
+ * Runs the decode (which also leaves each query head's log-sum-exp in the
+ * workspace) and then one small kernel that attends over the window and
+ * merges both parts into out.  Asynchronous, allocates nothing; errors as
+ * tq_paged_decode (TQ_ERR_WORKSPACE, before any launch, for a workspace
+ * below tq_hybrid_workspace_bytes). */
+tq_status tq_paged_decode_hybrid(const tq_ctx* ctx, const void* q, tq_dtype q_dtype,
+                                 int batch, int num_q_heads, int num_kv_heads,
+                                 const uint8_t* k_pages, int k_bits,
+                                 const uint8_t* v_pages, int v_bits,
+                                 int64_t num_blocks, int block_size,
+                                 const int32_t* block_table, int max_blocks_per_seq,
+                                 const int32_t* seq_lens, int max_seq_len,
+                                 const void* recent_k, const void* recent_v, tq_dtype recent_dtype,
+                                 int recent_cap, const int32_t* recent_lens, float scale,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* tq_paged_decode for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):

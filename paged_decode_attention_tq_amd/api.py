@@ -26,6 +26,8 @@ __all__ = [
     "decode_workspace_bytes",
     "decode_kernel",
     "paged_decode",
+    "hybrid_workspace_bytes",
+    "paged_decode_hybrid",
     "paged_decode_noalloc",
 ]
 
@@ -228,6 +230,57 @@ def paged_decode(ctx: Context, q: torch.Tensor, k_pages: torch.Tensor, v_pages: 
         seq_lens.data_ptr(), max_seq_len, float(scale) if scale else 0.0, out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
     check(st, "tq_paged_decode")
+    return out
+
+
+def hybrid_workspace_bytes(ctx: Context, batch, num_q_heads, num_kv_heads, max_seq_len, block_size=16) -> int:
+    return int(_lib.lib().tq_hybrid_workspace_bytes(ctx.handle, batch, num_q_heads, num_kv_heads,
+                                                    max_seq_len, block_size))
+
+
+def paged_decode_hybrid(ctx: Context, q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                        block_table: torch.Tensor, seq_lens: torch.Tensor, recent_k: torch.Tensor,
+                        recent_v: torch.Tensor, recent_lens: torch.Tensor, k_bits: int, v_bits: int,
+                        max_seq_len: int | None = None, scale: float | None = None,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode over packed history plus the exact recent window -> fp32 ``[B, Hq, d]``.
+
+    ``recent_k`` / ``recent_v``: ``[B, cap, Hkv, d]`` fp32/fp16/bf16;
+    ``recent_lens``: int32 ``[B]`` (rows used per sequence).
+    """
+    _need(q.is_cuda and q.dim() == 3 and q.shape[2] == ctx.head_dim and q.is_contiguous(), "q must be [B, Hq, d]")
+    _need(q.dtype in _DTYPES, "q dtype must be fp32/fp16/bf16")
+    B, Hq, d = q.shape
+    for name, pg, bits in (("k_pages", k_pages, k_bits), ("v_pages", v_pages, v_bits)):
+        _need(pg.dtype == torch.uint8 and pg.dim() == 4 and pg.is_contiguous(), f"{name} must be uint8 4-D")
+        _need(pg.shape[3] == row_bytes(d, bits), f"{name} row_bytes does not match bits")
+    NB, BS, Hkv, _ = k_pages.shape
+    _need(tuple(v_pages.shape[:3]) == (NB, BS, Hkv), "k_pages / v_pages geometry mismatch")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B
+          and block_table.is_contiguous(), "block_table must be int32 [B, max_blocks]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (B,), "seq_lens must be int32 [B]")
+    _need(recent_k.is_cuda and recent_v.is_cuda and recent_lens.is_cuda, "tensors must be on the GPU")
+    _need(recent_k.dim() == 4 and recent_k.shape[0] == B and tuple(recent_k.shape[2:]) == (Hkv, d)
+          and recent_k.is_contiguous(), "recent_k must be [B, cap, Hkv, d]")
+    _need(recent_v.shape == recent_k.shape and recent_v.dtype == recent_k.dtype and recent_v.is_contiguous(),
+          "recent_v must match recent_k")
+    _need(recent_k.dtype in _DTYPES, "recent dtype must be fp32/fp16/bf16")
+    _need(recent_lens.dtype == torch.int32 and recent_lens.shape == (B,), "recent_lens must be int32 [B]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out.dtype == torch.float32 and out.shape == (B, Hq, d) and out.is_contiguous(), "out must be fp32 [B, Hq, d]")
+    need = hybrid_workspace_bytes(ctx, B, Hq, Hkv, max_seq_len, BS)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = _lib.lib().tq_paged_decode_hybrid(
+        ctx.handle, q.data_ptr(), _DTYPES[q.dtype], B, Hq, Hkv, k_pages.data_ptr(), k_bits,
+        v_pages.data_ptr(), v_bits, NB, BS, block_table.data_ptr(), block_table.shape[1],
+        seq_lens.data_ptr(), max_seq_len, recent_k.data_ptr(), recent_v.data_ptr(), _DTYPES[recent_k.dtype],
+        recent_k.shape[1], recent_lens.data_ptr(), float(scale) if scale else 0.0, out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
+    check(st, "tq_paged_decode_hybrid")
     return out
 
 

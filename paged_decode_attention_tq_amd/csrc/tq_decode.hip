@@ -699,8 +699,9 @@ hipError_t launch_decode(const DecodeArgs& a, int k_bits, int v_bits, hipStream_
 // ===========================================================================
 // Merge: one wave per (b, h).  Combines the splits' normalised rotated sums by
 // their log2-sum-exp2, divides the value scale out, applies the inverse
-// rotation s * H y / sqrt(128) and writes fp32 out.  Lane l owns dims l and
-// l + 64; lane s holds the weight of split s (at most 64 splits).
+// rotation s * H y / sqrt(128) and writes fp32 out (and, when asked, the
+// sequence's log2-sum-exp2).  Lane l owns dims l and l + 64; lane s holds the
+// weight of split s (at most 64 splits).
 // ===========================================================================
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int tid = __builtin_amdgcn_workitem_id_x();
@@ -713,6 +714,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (L <= 0) {
     o[lane] = 0.0f;
     o[lane + 64] = 0.0f;
+    if (a.lse_out && lane == 0) a.lse_out[unit] = -__builtin_inff();
     return;
   }
   const int npages = (L + kBlockSize - 1) / kBlockSize;
@@ -750,6 +752,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const float inv = 1.0f / den;
   y0 *= inv;
   y1 *= inv;
+  if (a.lse_out && lane == 0) a.lse_out[unit] = M + __builtin_log2f(den);
   // H over 128 points: stage 64 inside the lane, stages 1..32 across lanes
   {
     const float u = y0, v = y1;

@@ -211,6 +211,8 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
       float* o = a.out + (int64_t)bb * Hq * kHeadDim;
       for (int i = lane; i < Hq * kHeadDim / 4; i += 64)
         *reinterpret_cast<floatx4*>(o + 4 * i) = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (a.lse_out)
+        for (int h = lane; h < Hq; h += 64) a.lse_out[(int64_t)bb * Hq + h] = -__builtin_inff();
     }
   }
   const long long r0 = share_point(T, wg, a.num_wg);
@@ -644,6 +646,7 @@ __global__ __launch_bounds__(64 * WaveCount<NH>::value) void decode_wave_kernel(
               uint32_t sw = pick4(a.sign_bits, d0 >> 5) >> (d0 & 31);  // the 16 signs of dims d0 .. d0 + 15
               asm volatile("" : "+v"(sw));  // (computed here, not hoisted and held across the walk)
               float* dst = a.out + ((int64_t)b * Hq + h) * kHeadDim + d0;
+              if (a.lse_out && (lane & 7) == 0) a.lse_out[(int64_t)b * Hq + h] = M + __builtin_log2f(lsum);
 #pragma unroll
               for (int jj = 0; jj < 16; jj += 4) {
                 floatx4 o4;
@@ -785,6 +788,7 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(WaveMergeArgs a) {
   if (pb <= 0) {
     o[lane] = 0.0f;
     o[lane + 64] = 0.0f;
+    if (a.lse_out && lane == 0) a.lse_out[unit] = -__builtin_inff();
     return;
   }
   const long long NW = a.num_wg;
@@ -843,6 +847,7 @@ __global__ __launch_bounds__(256) void merge_wave_kernel(WaveMergeArgs a) {
   const float inv = 1.0f / den;
   y0 *= inv;
   y1 *= inv;
+  if (a.lse_out && lane == 0) a.lse_out[unit] = M + __builtin_log2f(den);
   // H over 128 points: stage 64 inside the lane, stages 1..32 across lanes
   {
     const float u = y0, v = y1;

@@ -589,12 +589,18 @@ const char* tq_decode_kernel(int batch, int num_q_heads, int num_kv_heads, int m
   return nullptr;
 }
 
-tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
-                          int num_q_heads, int num_kv_heads, const uint8_t* k_pages, int k_bits,
-                          const uint8_t* v_pages, int v_bits, int64_t num_blocks, int block_size,
-                          const int32_t* block_table, int max_blocks_per_seq,
-                          const int32_t* seq_lens, int max_seq_len, float scale, float* out,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode of tq_paged_decode; lse_out (device [batch, num_q_heads] or
+// null) receives each query head's log2-sum-exp2 of its scores times log2(e)
+// (-inf for an empty sequence) where the output is finished.
+tq_status decode_impl(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch, int num_q_heads,
+                      int num_kv_heads, const uint8_t* k_pages, int k_bits, const uint8_t* v_pages, int v_bits,
+                      int64_t num_blocks, int block_size, const int32_t* block_table, int max_blocks_per_seq,
+                      const int32_t* seq_lens, int max_seq_len, float scale, float* out, float* lse_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   if (!ctx || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_seq_len < 0)
     return TQ_ERR_INVALID_ARG;
@@ -635,6 +641,7 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
     w.part_acc = static_cast<float*>(workspace);
     w.part_lse = w.part_acc + ((size_t)batch + wp.num_wg) * num_q_heads * kHeadDim;
     w.out = out;
+    w.lse_out = lse_out;
     w.direct = wp.num_wg == 1 ? 1 : 0;  // then every sequence is finished by the decode kernel
     w.k_page_bytes = (int64_t)block_size * num_kv_heads * k_row_bytes;
     w.v_page_bytes = (int64_t)block_size * num_kv_heads * v_row_bytes;
@@ -660,6 +667,7 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
     m.part_lse = w.part_lse;
     m.seq_lens = seq_lens;
     m.out = out;
+    m.lse_out = lse_out;
     m.batch = batch;
     m.num_q_heads = num_q_heads;
     m.num_wg = wp.num_wg;
@@ -735,6 +743,7 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   m.part_lse = d.part_lse;
   m.seq_lens = seq_lens;
   m.out = out;
+  m.lse_out = lse_out;
   m.batch = batch;
   m.num_q_heads = num_q_heads;
   m.pages_per_split = p.pages_per_split;
@@ -743,6 +752,69 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   m.inv_v_scale_over_sqrt_d = (float)(1.0 / ((double)v_scale * std::sqrt((double)kHeadDim)));
   std::memcpy(m.sign_bits, ctx->sign_bits, sizeof(m.sign_bits));
   return hip_status(tq::launch_merge(m, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
+                          int num_q_heads, int num_kv_heads, const uint8_t* k_pages, int k_bits,
+                          const uint8_t* v_pages, int v_bits, int64_t num_blocks, int block_size,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int32_t* seq_lens, int max_seq_len, float scale, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(ctx, q, q_dtype, batch, num_q_heads, num_kv_heads, k_pages, k_bits, v_pages, v_bits,
+                     num_blocks, block_size, block_table, max_blocks_per_seq, seq_lens, max_seq_len, scale, out,
+                     nullptr, workspace, workspace_bytes, stream);
+}
+
+size_t tq_hybrid_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads, int num_kv_heads,
+                                 int max_seq_len, int block_size) {
+  const size_t dec = tq_decode_workspace_bytes(ctx, batch, num_q_heads, num_kv_heads, max_seq_len, block_size);
+  if (dec == 0) return 0;
+  return ((dec + 255) & ~(size_t)255) + (size_t)batch * num_q_heads * sizeof(float);
+}
+
+tq_status tq_paged_decode_hybrid(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
+                                 int num_q_heads, int num_kv_heads, const uint8_t* k_pages, int k_bits,
+                                 const uint8_t* v_pages, int v_bits, int64_t num_blocks, int block_size,
+                                 const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                                 int max_seq_len, const void* recent_k, const void* recent_v,
+                                 tq_dtype recent_dtype, int recent_cap, const int32_t* recent_lens, float scale,
+                                 float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || recent_cap < 0) return TQ_ERR_INVALID_ARG;
+  if (recent_dtype != TQ_F32 && recent_dtype != TQ_F16 && recent_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (batch == 0) return TQ_OK;
+  if (recent_cap > 0 && (!recent_k || !recent_v || !recent_lens)) return TQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(recent_k) | reinterpret_cast<uintptr_t>(recent_v)) & 15) return TQ_ERR_ALIGNMENT;
+  const size_t need = tq_hybrid_workspace_bytes(ctx, batch, num_q_heads, num_kv_heads, max_seq_len, block_size);
+  if (!workspace || need == 0 || workspace_bytes < need) return TQ_ERR_WORKSPACE;
+  const size_t dec = (tq_decode_workspace_bytes(ctx, batch, num_q_heads, num_kv_heads, max_seq_len, block_size) +
+                      255) & ~(size_t)255;
+  float* lse = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + dec);
+  tq_status st = decode_impl(ctx, q, q_dtype, batch, num_q_heads, num_kv_heads, k_pages, k_bits, v_pages, v_bits,
+                             num_blocks, block_size, block_table, max_blocks_per_seq, seq_lens, max_seq_len, scale,
+                             out, lse, workspace, dec, stream);
+  if (st != TQ_OK || recent_cap == 0) return st;
+  tq::HybridArgs h;
+  std::memset(&h, 0, sizeof(h));
+  h.q = q;
+  h.recent_k = recent_k;
+  h.recent_v = recent_v;
+  h.recent_lens = recent_lens;
+  h.lse = lse;
+  h.out = out;
+  h.batch = batch;
+  h.num_q_heads = num_q_heads;
+  h.num_kv_heads = num_kv_heads;
+  h.group = num_q_heads / num_kv_heads;
+  h.cap = recent_cap;
+  h.q_dtype = (int)q_dtype;
+  h.r_dtype = (int)recent_dtype;
+  const float sm_scale = scale > 0 ? scale : 1.0f / std::sqrt((float)kHeadDim);
+  h.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  return hip_status(tq::launch_hybrid(h, (hipStream_t)stream));
 }
 
 tq_status tq_paged_decode_noalloc(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,

@@ -119,6 +119,7 @@ struct WaveArgs {
   float* part_acc;               // [B + num_wg - 1, Hq, 128] rotated, normalised, x v_scale
   float* part_lse;               // [B + num_wg - 1, Hq]      log2-sum-exp2 of the segment
   float* out;                    // [B, Hq, 128]: written here for every sequence whose pages one workgroup holds
+  float* lse_out;                // [B, Hq] or null: log2-sum-exp2 of the scores wherever out is written (-inf: empty)
   int64_t k_page_bytes;
   int64_t v_page_bytes;
   int64_t num_blocks;            // block ids outside [0, num_blocks) read as zero rows
@@ -146,6 +147,7 @@ struct WaveMergeArgs {
   const float* part_lse;
   const int32_t* seq_lens;
   float* out;                    // [B, Hq, 128]
+  float* lse_out;                // [B, Hq] or null: log2-sum-exp2 of the sequence's scores (-inf: empty)
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_wg;
@@ -154,12 +156,34 @@ struct WaveMergeArgs {
   uint32_t sign_bits[kHeadDim / 32];
 };
 
+// Arguments of the recent-window kernel of the hybrid decode
+// (tq_hybrid.hip): one workgroup per (sequence, KV head, group of up to 8
+// query heads) attends over the sequence's dense window rows and merges the
+// result with the packed part's finished output by the two log2-sum-exp2s.
+struct HybridArgs {
+  const void* q;                 // [B, Hq, 128] of q_dtype
+  const void* recent_k;          // [B, cap, Hkv, 128] of r_dtype
+  const void* recent_v;
+  const int32_t* recent_lens;    // [B], clamped to 0..cap
+  const float* lse;              // [B, Hq] packed part's log2-sum-exp2 (-inf: no packed token)
+  float* out;                    // [B, Hq, 128]: the packed part's output in, the merged output out
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t cap;
+  int32_t q_dtype;
+  int32_t r_dtype;
+  float scale_log2;              // softmax scale * log2(e)
+};
+
 // Arguments of the split-merge + inverse-rotation kernel.
 struct MergeArgs {
   const float* part_acc;
   const float* part_lse;
   const int32_t* seq_lens;
   float* out;                    // [B, Hq, 128]
+  float* lse_out;                // [B, Hq] or null: log2-sum-exp2 of the sequence's scores (-inf: empty)
   int32_t batch;
   int32_t num_q_heads;
   int32_t pages_per_split;
@@ -184,6 +208,7 @@ bool wave_fits(int k_bits, int v_bits, int nh, int num_kv_heads);
 int wave_waves(int nh);                           // waves per workgroup (0: not built)
 hipError_t launch_decode_wave(const WaveArgs& a, int k_bits, int v_bits, int nh, hipStream_t stream);
 hipError_t launch_merge_wave(const WaveMergeArgs& a, hipStream_t stream);
+hipError_t launch_hybrid(const HybridArgs& a, hipStream_t stream);
 
 // the static scratch of tq_paged_decode_noalloc (tq_scratch.hip): its size, and
 // its device address on the current device (looked up once per device; nullptr

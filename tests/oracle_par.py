@@ -79,3 +79,29 @@ def sequence_outputs(codec, w, b, k_pages, v_pages, queries):
     with ThreadPoolExecutor(min(_threads(), Hkv)) as ex:
         parts = list(ex.map(job, range(Hkv)))
     return np.concatenate(parts)
+
+
+def sequence_hybrid_outputs(codec, w, b, k_pages, v_pages, queries, recent_k, recent_v, recent_len):
+    """``oracle.paged_decode_hybrid`` outputs ``[Hq, d]`` of sequence ``b`` from
+    its own pages (identity block table) and its window rows ``[cap, Hkv, d]``,
+    one KV head (its pages' and window's head slice, its query group) per
+    thread."""
+    L = int(w.seq_lens[b])
+    Hq, Hkv = w.num_q_heads, w.num_kv_heads
+    G = Hq // Hkv
+    npg = k_pages.shape[0]
+    bt = np.arange(max(npg, 1), dtype=np.int32)[None]
+    ck, cv = codec.centroids32(w.k_bits), codec.centroids32(w.v_bits)
+
+    def job(g):
+        kp = np.ascontiguousarray(k_pages[:, :, g:g + 1])
+        vp = np.ascontiguousarray(v_pages[:, :, g:g + 1])
+        q = queries[b][None, g * G:(g + 1) * G]
+        return oracle.paged_decode_hybrid(q, kp, vp, bt, np.array([L]), recent_k[None, :, g:g + 1],
+                                          recent_v[None, :, g:g + 1], np.array([recent_len]), w.k_bits, w.v_bits,
+                                          codec.signs, ck, cv)[0]
+
+    with ThreadPoolExecutor(min(_threads(), Hkv)) as ex:
+        parts = list(ex.map(job, range(Hkv)))
+    return np.concatenate(parts).astype(np.float64)
+

@@ -79,7 +79,18 @@ def test_status_strings_and_argument_errors():
     assert rd(h, a64, 4, 16, 2, 4, ctypes.c_void_p(68), 5, a64, 0, None, None) == 3  # slots not 8-byte aligned
     assert rd(h, a64, 4, 16, 2, 4, a64, 5, ctypes.c_void_p(72), 0, None, None) == 3  # out not 16-byte aligned
     assert rd(h, a64, 4, 16, 2, 4, a64, 1 << 30, a64, 0, None, None) == 2  # 2^31 rows
+    # the hybrid decode: its own checks, then the decode's
+    hy = lib.tq_paged_decode_hybrid
     p = ctypes.c_void_p(16)
+    need = lib.tq_hybrid_workspace_bytes(h, 2, 8, 2, 64, 16)
+    assert need >= lib.tq_decode_workspace_bytes(h, 2, 8, 2, 64, 16) + 2 * 8 * 4
+    assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, p, p, 7, 16, p, 0.0, p, p, need, None) == 1  # dtype
+    assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, None, p, 1, 16, p, 0.0, p, p, need, None) == 1  # null window
+    assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, ctypes.c_void_p(24), p, 1, 16, p, 0.0, p, p, need,
+              None) == 3  # window not 16-byte aligned
+    assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, p, p, 1, 16, p, 0.0, p, p, need - 4, None) == 4
+    assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, p, p, 1, -1, p, 0.0, p, p, need, None) == 1  # cap < 0
+    assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 32, p, 4, p, 64, p, p, 1, 16, p, 0.0, p, p, need, None) == 2  # block 32
     args = dict(batch=2, hq=128, hkv=1)  # group 128 > 64
     assert lib.tq_paged_decode(h, p, 1, 2, 128, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 2
     assert lib.tq_paged_decode(h, p, 1, 2, 6, 4, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 1
