@@ -17,23 +17,41 @@ namespace tq {
 
 namespace {
 
-constexpr int kChunk = 64;   // window tokens staged per round
+constexpr int kChunk = 64;   // window tokens per round
 constexpr int kRow = 132;    // floats per staged row: 16-byte aligned, neighbouring rows on other banks
 constexpr int kHeads = 8;    // query heads per workgroup
+constexpr int kPer = kChunk * 32 / 256;  // (token, dim quad) slots per thread per round
 
-// Four consecutive elements of a row of fp32 / fp16 / bf16 values, widened to fp32.
-__device__ __forceinline__ floatx4 load4(const void* base, int64_t elem, int dt) {
-  if (dt == 0) {
+// Raw words of four consecutive elements (fp32: 4 words; fp16 / bf16: 2).
+template <int RDT>
+struct Quad {
+  uint32_t w[RDT == 0 ? 4 : 2];
+};
+
+template <int RDT>
+__device__ __forceinline__ Quad<RDT> load_quad(const void* base, int64_t elem) {
+  Quad<RDT> r;
+  if constexpr (RDT == 0) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + elem);
-    return floatx4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+    r.w[0] = v.x, r.w[1] = v.y, r.w[2] = v.z, r.w[3] = v.w;
+  } else {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + elem);
+    r.w[0] = v.x, r.w[1] = v.y;
   }
-  const u32x2 v = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + elem);
-  if (dt == 1) {
-    const half4 h = __builtin_bit_cast(half4, v);
+  return r;
+}
+
+template <int RDT>
+__device__ __forceinline__ floatx4 widen(const Quad<RDT>& r) {
+  if constexpr (RDT == 0) {
+    return floatx4{__uint_as_float(r.w[0]), __uint_as_float(r.w[1]), __uint_as_float(r.w[2]), __uint_as_float(r.w[3])};
+  } else if constexpr (RDT == 1) {
+    const half4 h = __builtin_bit_cast(half4, u32x2{r.w[0], r.w[1]});
     return floatx4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+  } else {
+    return floatx4{bf16_to_f32((uint16_t)r.w[0]), bf16_to_f32((uint16_t)(r.w[0] >> 16)), bf16_to_f32((uint16_t)r.w[1]),
+                   bf16_to_f32((uint16_t)(r.w[1] >> 16))};
   }
-  return floatx4{bf16_to_f32((uint16_t)v.x), bf16_to_f32((uint16_t)(v.x >> 16)), bf16_to_f32((uint16_t)v.y),
-                 bf16_to_f32((uint16_t)(v.y >> 16))};
 }
 
 __device__ __forceinline__ float load1(const void* base, int64_t elem, int dt) {
@@ -45,17 +63,22 @@ __device__ __forceinline__ float load1(const void* base, int64_t elem, int dt) {
 }  // namespace
 
 // One workgroup of 256 threads per (sequence b, KV head g, group of up to 8
-// query heads).  Per round of up to 64 window tokens: the K and V rows are
-// staged in LDS as fp32; thread pairs (head, token) form the scores; the 32
-// threads of each head (thread = head * 32 + dim quad) update its running
-// maximum, normaliser and 4 output dims (online softmax in the log2 domain).
+// query heads).  Rounds of 64 window tokens: each thread holds 8 (token, dim
+// quad) pieces of the round's K and V rows in registers (the next round's
+// are loaded while the current one is computed), writes them to LDS as
+// fp32 (zeros past the window), and then
+//   * scores: lane t of wave w forms token t's scores for heads w and w + 4;
+//   * softmax and values: the 32 threads of head i (thread = 32 i + dim quad)
+//     update its running maximum and normaliser and 4 output dims over the
+//     64 tokens (online softmax in the log2 domain).
 // Finally the window's part is merged with the packed part's output.
+template <int RDT>
 __global__ __launch_bounds__(256) void hybrid_window_kernel(HybridArgs a) {
   __shared__ float ks[kChunk * kRow];
   __shared__ float vs[kChunk * kRow];
   __shared__ float qs[kHeads * 128];
   __shared__ float ps[kHeads * kChunk];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group, Hkv = a.num_kv_heads;
   const int nhc = (G + kHeads - 1) / kHeads;
   int wg = blockIdx.x;
@@ -66,45 +89,57 @@ __global__ __launch_bounds__(256) void hybrid_window_kernel(HybridArgs a) {
   const int R = min(max(a.recent_lens[b], 0), a.cap);
   if (R == 0) return;  // the packed part's output stands (uniform per workgroup)
 
-  for (int e = tid; e < nh * 128; e += 256)
-    qs[e] = load1(a.q, ((int64_t)b * a.num_q_heads + h0) * 128 + e, a.q_dtype);
+  const int hi = tid >> 5, dq = tid & 31;  // head and dim quad (values); also the first staged token
+  const int64_t row_stride = (int64_t)Hkv * 128;  // elements between tokens of one head
+  const int64_t base = ((int64_t)b * a.cap * Hkv + g) * 128 + 4 * dq;
+  Quad<RDT> kq[kPer], vq[kPer];
+  auto fetch = [&](int c0) {  // tokens c0 + hi + 8 j, dims 4 dq .. 4 dq + 3
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int t = c0 + hi + 8 * j;
+      if (t < R) {
+        kq[j] = load_quad<RDT>(a.recent_k, base + t * row_stride);
+        vq[j] = load_quad<RDT>(a.recent_v, base + t * row_stride);
+      } else {
+#pragma unroll
+        for (int u = 0; u < (RDT == 0 ? 4 : 2); ++u) kq[j].w[u] = vq[j].w[u] = 0u;
+      }
+    }
+  };
+  fetch(0);
+  for (int e = tid; e < kHeads * 128; e += 256)
+    qs[e] = e < nh * 128 ? load1(a.q, ((int64_t)b * a.num_q_heads + h0) * 128 + e, a.q_dtype) : 0.0f;
 
-  const int hi = tid >> 5, dq = tid & 31;  // this thread's head and dims 4 dq .. 4 dq + 3
   float m = -__builtin_inff(), l = 0.0f;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int64_t row_stride = (int64_t)Hkv * 128;  // elements between tokens of one head
-  const int64_t base = ((int64_t)b * a.cap * Hkv + g) * 128;
   for (int c0 = 0; c0 < R; c0 += kChunk) {
-    const int n = min(kChunk, R - c0);
     __syncthreads();  // the previous round's reads of ks / vs / ps are done (and qs is written)
-    for (int e = tid; e < n * 32; e += 256) {
-      const int t = e >> 5, d4 = 4 * (e & 31);
-      const int64_t at = base + (int64_t)(c0 + t) * row_stride + d4;
-      *reinterpret_cast<floatx4*>(ks + t * kRow + d4) = load4(a.recent_k, at, a.r_dtype);
-      *reinterpret_cast<floatx4*>(vs + t * kRow + d4) = load4(a.recent_v, at, a.r_dtype);
-    }
-    __syncthreads();
-    // scores, in log2 units: pair p = tid + 256 k -> (head p / 64, token p % 64)
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int p = tid + 256 * k, i = p >> 6, t = p & 63;
-      float s = -__builtin_inff();
-      if (i < nh && t < n) {
-        const float* qr = qs + i * 128;
-        const float* kr = ks + t * kRow;
-        float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < 128; d += 4) {
-          const floatx4 qv = *reinterpret_cast<const floatx4*>(qr + d);
-          const floatx4 kv = *reinterpret_cast<const floatx4*>(kr + d);
-          d0 = fmaf(qv[0], kv[0], d0);
-          d1 = fmaf(qv[1], kv[1], d1);
-          d2 = fmaf(qv[2], kv[2], d2);
-          d3 = fmaf(qv[3], kv[3], d3);
-        }
-        s = ((d0 + d1) + (d2 + d3)) * a.scale_log2;
+    for (int j = 0; j < kPer; ++j) {
+      const int t = hi + 8 * j;
+      *reinterpret_cast<floatx4*>(ks + t * kRow + 4 * dq) = widen<RDT>(kq[j]);
+      *reinterpret_cast<floatx4*>(vs + t * kRow + 4 * dq) = widen<RDT>(vq[j]);
+    }
+    if (c0 + kChunk < R) fetch(c0 + kChunk);  // in flight during this round's work
+    __syncthreads();
+    {
+      // scores in log2 units; past the window -inf
+      const int i0 = wave, i1 = wave + 4, t = lane;
+      const float* kr = ks + t * kRow;
+      float s0a = 0.f, s0b = 0.f, s1a = 0.f, s1b = 0.f;
+#pragma unroll
+      for (int d = 0; d < 128; d += 4) {
+        const floatx4 kv = *reinterpret_cast<const floatx4*>(kr + d);
+        const floatx4 q0 = *reinterpret_cast<const floatx4*>(qs + i0 * 128 + d);
+        const floatx4 q1 = *reinterpret_cast<const floatx4*>(qs + i1 * 128 + d);
+        s0a = fmaf(q0[0], kv[0], fmaf(q0[1], kv[1], s0a));
+        s0b = fmaf(q0[2], kv[2], fmaf(q0[3], kv[3], s0b));
+        s1a = fmaf(q1[0], kv[0], fmaf(q1[1], kv[1], s1a));
+        s1b = fmaf(q1[2], kv[2], fmaf(q1[3], kv[3], s1b));
       }
-      ps[p] = s;
+      const bool in = c0 + t < R;
+      ps[i0 * kChunk + t] = in ? (s0a + s0b) * a.scale_log2 : -__builtin_inff();
+      ps[i1 * kChunk + t] = in ? (s1a + s1b) * a.scale_log2 : -__builtin_inff();
     }
     __syncthreads();
     if (hi < nh) {
@@ -130,10 +165,10 @@ __global__ __launch_bounds__(256) void hybrid_window_kernel(HybridArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const float* pr = ps + hi * kChunk;
-      for (int t = 0; t < n; ++t) {
-        const float w = pr[t];
+#pragma unroll
+      for (int t = 0; t < kChunk; ++t) {  // rows past the window are zero, with weight 0
         const floatx4 v = *reinterpret_cast<const floatx4*>(vs + t * kRow + 4 * dq);
-        acc += w * v;
+        acc += pr[t] * v;
       }
     }
   }
@@ -154,7 +189,13 @@ hipError_t launch_hybrid(const HybridArgs& a, hipStream_t stream) {
   const int nhc = (a.group + kHeads - 1) / kHeads;
   const long long wgs = (long long)a.batch * a.num_kv_heads * nhc;
   if (wgs == 0) return hipSuccess;
-  hipLaunchKernelGGL(hybrid_window_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)wgs), block(256);
+  if (a.r_dtype == 0)
+    hipLaunchKernelGGL(hybrid_window_kernel<0>, grid, block, 0, stream, a);
+  else if (a.r_dtype == 1)
+    hipLaunchKernelGGL(hybrid_window_kernel<1>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(hybrid_window_kernel<2>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
