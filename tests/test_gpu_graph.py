@@ -23,9 +23,11 @@ def ctx():
     return api.Context(128, 42)
 
 
-# wave-private (with its merge kernel), wave-private as one workgroup (no
-# merge kernel), staged
-@pytest.mark.parametrize("hkv,G,lens", [(2, 8, [700, 33, 1500]), (1, 2, [64, 17, 0]), (8, 8, [700, 33, 1500])])
+# wave-private split over workgroups (with its merge kernel; the second case
+# with an empty sequence), wave-private as one workgroup (no merge kernel),
+# staged
+@pytest.mark.parametrize("hkv,G,lens", [(2, 8, [2100, 33, 1500]), (2, 8, [700, 33, 0]), (1, 2, [64, 17, 0]),
+                                        (8, 8, [700, 33, 1500])])
 def test_graph_replays_equal_eager(ctx, hkv, G, lens):
     w = workloads.make_workload(f"graph{hkv}", num_q_heads=hkv * G, num_kv_heads=hkv, seq_lens=lens, seed=40 + hkv)
     kernel = api.decode_kernel(w.batch, w.num_q_heads, hkv, w.max_seq_len, 4, 4)
