@@ -43,7 +43,7 @@ from .codec import (
     decompress_kv,
     OracleCodec,
 )
-from .attention import paged_decode, paged_decode_heads, paged_decode_hybrid
+from .attention import paged_decode, paged_decode_heads, paged_decode_hybrid, paged_prefill
 
 __all__ = [
     "beta_codebook",
@@ -68,4 +68,5 @@ __all__ = [
     "paged_decode",
     "paged_decode_heads",
     "paged_decode_hybrid",
+    "paged_prefill",
 ]

@@ -26,7 +26,7 @@ import numpy as np
 
 from .codec import dequantize_rows
 
-__all__ = ["gather_rows", "paged_decode", "paged_decode_heads", "paged_decode_hybrid"]
+__all__ = ["gather_rows", "paged_decode", "paged_decode_heads", "paged_decode_hybrid", "paged_prefill"]
 
 
 def gather_rows(pages, block_table_row, length, kv_head):
@@ -128,5 +128,44 @@ def paged_decode_hybrid(q, k_pages, v_pages, block_table, seq_lens, recent_k, re
             V = np.concatenate([V, rv[b, :R, g]], axis=0)
             for h in range(g * G, (g + 1) * G):
                 out[b, h] = _attend(q[b, h].astype(np.float64), K, V, scale)
+    return out.astype(np.float32)
+
+
+def paged_prefill(q, q_lens, k_pages, v_pages, block_table, seq_lens, k_bits, v_bits, signs, ck32, cv32,
+                  scale=None):
+    """Several query tokens per sequence over the packed pages, causal -> float32 ``[B, Lq, Hq, d]``.
+
+    Sources: "vLLM Usage", "Runtime Dispatch" (with a cache present, mixed
+    prefill / decode batches attend through the packed cache) and
+    "Architecture", "Cache Lifecycle" (prefill, then decode, over the
+    compressed store).
+
+    Readings: ``q[b, j]`` for ``j < q_lens[b]`` are the queries of the last
+    ``q_lens[b]`` tokens of sequence b, whose K/V rows are already in the
+    pages (the cache is updated before attention); query j sits at position
+    ``P_b + j`` with ``P_b = seq_lens[b] - q_lens[b]`` and attends tokens
+    ``0 .. P_b + j`` (causal within the chunk), rows reconstructed as in
+    ``paged_decode``.  Rows ``j >= q_lens[b]`` are zeros.  ``q_lens[b]`` must
+    lie in ``0 .. min(Lq, seq_lens[b])``.
+    """
+    q = np.asarray(q)
+    B, Lq, Hq, d = q.shape
+    Hkv = k_pages.shape[2]
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    out = np.zeros((B, Lq, Hq, d), dtype=np.float64)
+    for b in range(B):
+        L, n = int(seq_lens[b]), int(q_lens[b])
+        if not 0 <= n <= min(Lq, L):
+            raise ValueError("query length outside 0 .. min(Lq, seq_len)")
+        if n == 0:
+            continue
+        P = L - n
+        for g in range(Hkv):
+            K = dequantize_rows(gather_rows(k_pages, block_table[b], L, g), k_bits, d, signs, ck32)
+            V = dequantize_rows(gather_rows(v_pages, block_table[b], L, g), v_bits, d, signs, cv32)
+            for j in range(n):
+                for h in range(g * G, (g + 1) * G):
+                    out[b, j, h] = _attend(q[b, j, h].astype(np.float64), K[: P + j + 1], V[: P + j + 1], scale)
     return out.astype(np.float32)
 
