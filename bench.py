@@ -247,9 +247,11 @@ def main():
     ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush (1 GiB write, then 1 GiB read) before each timed step")
-    ap.add_argument("--op", choices=("decode", "decompress", "hybrid"), default="decode",
+    ap.add_argument("--op", choices=("decode", "decompress", "hybrid", "prefill"), default="decode",
                     help="decode: the decode step (default); decompress: the dense readback of every K row; "
-                         "hybrid: the decode step over the packed pages plus an exact fp16 window per sequence")
+                         "hybrid: the decode step over the packed pages plus an exact fp16 window per sequence; "
+                         "prefill: a chunk of --q-len queries per sequence attending causally over the pages")
+    ap.add_argument("--q-len", type=int, default=8, help="queries per sequence (--op prefill)")
     ap.add_argument("--window", type=int, default=128, help="recent-window rows per sequence (--op hybrid)")
     ap.add_argument("--out-dtype", choices=("fp16", "bf16", "fp32"), default="fp16",
                     help="output dtype of the dense readback (--op decompress)")
@@ -266,7 +268,8 @@ def main():
 
     dev = torch.device("cuda:0")
     w = workloads.preset(args.config)
-    kernel = api.decode_kernel(w.batch, w.num_q_heads, w.num_kv_heads, w.max_seq_len, w.k_bits, w.v_bits)
+    kernel = api.decode_kernel(w.batch, w.num_q_heads * (args.q_len if args.op == "prefill" else 1), w.num_kv_heads,
+                               w.max_seq_len, w.k_bits, w.v_bits)
     B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
     log(f"[bench] {w.name}: B={B} L={w.max_seq_len} Hq={Hq} Hkv={Hkv} K{w.k_bits}V{w.v_bits} "
         f"packed={w.packed_kv_bytes() / 1e9:.3f} GB, {kernel} decode kernel")
@@ -318,7 +321,18 @@ def main():
     lens = torch.from_numpy(w.seq_lens).to(dev)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     hybrid = args.op == "hybrid"
-    if hybrid:
+    prefill = args.op == "prefill"
+    if prefill:
+        # the last q_len tokens of every sequence query the pages (their rows are
+        # rewritten each step like the decode step's new token)
+        Lq = args.q_len
+        pq = torch.from_numpy(np.random.default_rng(5).standard_normal((B, Lq, Hq, d), dtype=np.float32)).to(
+            device=dev, dtype=torch.float16)
+        ql_d = torch.full((B,), Lq, dtype=torch.int32, device=dev)
+        out = torch.empty((B, Lq, Hq, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(api.prefill_workspace_bytes(ctx, B, Lq, Hq, Hkv, w.max_seq_len), dtype=torch.uint8,
+                         device=dev)
+    elif hybrid:
         # a full window of exact rows per sequence, fp16, drawn like the workload's rows
         rl = np.full(B, args.window, dtype=np.int32)
         rk, rv = w.recent_window(args.window, rl, seed=1)
@@ -349,7 +363,10 @@ def main():
         api.write_kv_pair(ctx, k_new, v_new, kp, vp, new_slots, w.k_bits, w.v_bits, err_count=err, check_slots=False)
         if i is not None:
             ev[i][1].record()
-        if hybrid:
+        if prefill:
+            api.paged_prefill(ctx, pq, ql_d, kp, vp, bt, lens, w.k_bits, w.v_bits, max_seq_len=w.max_seq_len,
+                              out=out, workspace=ws)
+        elif hybrid:
             api.paged_decode_hybrid(ctx, q_d, kp, vp, bt, lens, rk_d, rv_d, rl_d, w.k_bits, w.v_bits,
                                     max_seq_len=w.max_seq_len, out=out, workspace=ws)
         else:
@@ -382,10 +399,12 @@ def main():
     dec_s = float(dec_ms.mean()) / 1e3
     achieved = packed / dec_s / 1e9
     result = {
-        "metric": ("paged TQ decode tokens/s + packed-KV HBM GB/s (% of peak), 1 MI355X" if not hybrid else
-                   f"paged TQ hybrid decode (packed history + {args.window}-row exact fp16 window) tokens/s + "
-                   "HBM GB/s (% of peak), 1 MI355X"),
-        "value": B / (ms_step / 1e3),
+        "metric": ("paged TQ decode tokens/s + packed-KV HBM GB/s (% of peak), 1 MI355X" if not (hybrid or prefill)
+                   else f"paged TQ hybrid decode (packed history + {args.window}-row exact fp16 window) tokens/s + "
+                   "HBM GB/s (% of peak), 1 MI355X" if hybrid else
+                   f"paged TQ multi-query attention ({args.q_len} causal queries per sequence) query tokens/s + "
+                   "packed-KV HBM GB/s (% of peak), 1 MI355X"),
+        "value": B * (args.q_len if prefill else 1) / (ms_step / 1e3),
         "unit": "decode tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -400,7 +419,8 @@ def main():
         "config": {
             "workload": f"{w.name}: batch {B} x {w.max_seq_len} tokens, Hq {Hq}, Hkv {Hkv}, head_dim {d}, "
                         f"block 16, K{w.k_bits}/V{w.v_bits}" +
-                        (f", plus a {args.window}-row fp16 window per sequence" if hybrid else ""),
+                        (f", plus a {args.window}-row fp16 window per sequence" if hybrid else "") +
+                        (f", {args.q_len} fp16 queries per sequence" if prefill else ""),
             "global_batch": B,
             "seq_len": w.max_seq_len,
             "parallelism": "single GPU",
@@ -416,12 +436,13 @@ def main():
             "bound": "hbm",
             "kernel": ((f"tq_paged_decode, {kernel} decode kernel + merge kernel" if kernel != "wave1" else
                         "tq_paged_decode, wave decode kernel as one workgroup (no merge kernel)") +
-                       (" + hybrid_window_kernel" if hybrid else "")),
+                       (" + hybrid_window_kernel" if hybrid else "") +
+                       (" + layout, tail readback and causal window kernels" if prefill else "")),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None if hybrid else traffic_bytes(w.name),
+            "traffic": None if (hybrid or prefill) else traffic_bytes(w.name),
         },
         "prefill_write": write,
         "stream_read_ceiling": None,
@@ -433,7 +454,7 @@ def main():
             f"{result['stream_read_ceiling']['mean_gbps']:.0f} GB/s mean")
     if hybrid:
         result["window_bytes"] = window_bytes
-    if not args.no_cpu_baseline and not hybrid:
+    if not args.no_cpu_baseline and not hybrid and not prefill:
         log("[bench] timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(w, kraw, vraw, q, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -4,7 +4,8 @@
  *
  * The library writes K/V rows into uint8 pages in the TQ row format, reads
  * them back as dense rows, and runs single-query paged decode attention over
- * those pages, alone or together with an exact window of recent rows.  Everything below is
+ * those pages, alone or together with an exact window of recent rows, and
+ * multi-query (prefill / verify) attention over them.  Everything below is
  * plain C: device buffers are raw device pointers, streams are hipStream_t
  * passed as void*.  The library never allocates device memory inside
  * tq_write_kv / tq_paged_decode and never synchronises the stream; the caller
@@ -261,6 +262,44 @@ tq_status tq_paged_decode_hybrid(const tq_ctx* ctx, const void* q, tq_dtype q_dt
                                  int recent_cap, const int32_t* recent_lens, float scale,
                                  float* out, void* workspace, size_t workspace_bytes,
                                  void* stream);
+
+/* Bytes of device workspace tq_paged_prefill needs for these sizes (sized
+ * for fp32 queries, enough for every query dtype).  The count of splits of
+ * its decode follows the current device's compute units, as in
+ * tq_decode_workspace_bytes.  0 for a non-positive batch, q_len or head
+ * count or a negative length. */
+size_t tq_prefill_workspace_bytes(const tq_ctx* ctx, int batch, int q_len, int num_q_heads,
+                                  int num_kv_heads, int max_seq_len, int block_size);
+
+/* Several query tokens per sequence over the packed pages, causal within the
+ * chunk ("vLLM Usage", "Runtime Dispatch": with a cache present, mixed
+ * prefill / decode batches attend through the packed cache): chunked
+ * prefill, speculative verification, mixed batches.  The queries of
+ * sequence b are those of its last q_lens[b] tokens, whose K/V rows are
+ * already written to the pages; query j sits at position
+ * P + j, P = seq_lens[b] - q_lens[b], and attends tokens 0 .. P + j.
+ *   q           device, [batch, q_len, num_q_heads, head_dim] of q_dtype,
+ *               contiguous, 16-byte aligned; rows j >= q_lens[b] are ignored.
+ *   q_lens      device, int32 [batch], each clamped to 0 .. min(q_len,
+ *               seq_lens[b]).
+ *   out         device, fp32 [batch, q_len, num_q_heads, head_dim],
+ *               16-byte aligned; rows j >= q_lens[b] are written as zeros.
+ *   workspace   device, >= tq_prefill_workspace_bytes(...) bytes, 256-byte
+ *               aligned; contents are scratch.
+ *   the rest    as tq_paged_decode.
+ * (num_q_heads / num_kv_heads) * q_len must be at most 64
+ * (TQ_ERR_UNSUPPORTED otherwise).  The prefix 0 .. P is read once for all of
+ * a sequence's queries: they are decoded together as q_len times as many
+ * query heads; the chunk's other tokens are read back densely and attended
+ * causally, and the two parts are merged by their log-sum-exps.
+ * Asynchronous, allocates nothing; errors as tq_paged_decode. */
+tq_status tq_paged_prefill(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch, int q_len,
+                           const int32_t* q_lens, int num_q_heads, int num_kv_heads,
+                           const uint8_t* k_pages, int k_bits, const uint8_t* v_pages, int v_bits,
+                           int64_t num_blocks, int block_size,
+                           const int32_t* block_table, int max_blocks_per_seq,
+                           const int32_t* seq_lens, int max_seq_len, float scale,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* tq_paged_decode for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):

@@ -69,6 +69,15 @@ SIGNATURES = {
          _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_void_p, _c.c_float,
          _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p],
     ),
+    "tq_prefill_workspace_bytes": (
+        _c.c_size_t, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
+    "tq_paged_prefill": (
+        _c.c_int,
+        [_c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_int, _c.c_int,
+         _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int,
+         _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_float,
+         _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p],
+    ),
     "tq_paged_decode_noalloc": (
         _c.c_int,
         [_c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,

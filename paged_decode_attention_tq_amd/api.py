@@ -28,6 +28,8 @@ __all__ = [
     "paged_decode",
     "hybrid_workspace_bytes",
     "paged_decode_hybrid",
+    "prefill_workspace_bytes",
+    "paged_prefill",
     "paged_decode_noalloc",
 ]
 
@@ -281,6 +283,52 @@ def paged_decode_hybrid(ctx: Context, q: torch.Tensor, k_pages: torch.Tensor, v_
         recent_k.shape[1], recent_lens.data_ptr(), float(scale) if scale else 0.0, out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
     check(st, "tq_paged_decode_hybrid")
+    return out
+
+
+def prefill_workspace_bytes(ctx: Context, batch, q_len, num_q_heads, num_kv_heads, max_seq_len,
+                            block_size=16) -> int:
+    return int(_lib.lib().tq_prefill_workspace_bytes(ctx.handle, batch, q_len, num_q_heads, num_kv_heads,
+                                                     max_seq_len, block_size))
+
+
+def paged_prefill(ctx: Context, q: torch.Tensor, q_lens: torch.Tensor, k_pages: torch.Tensor,
+                  v_pages: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, k_bits: int,
+                  v_bits: int, max_seq_len: int | None = None, scale: float | None = None,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Multi-query attention, causal within each sequence's last ``q_lens[b]``
+    tokens -> fp32 ``[B, Lq, Hq, d]`` (rows past ``q_lens[b]`` are zeros).
+
+    ``q``: ``[B, Lq, Hq, d]`` fp32/fp16/bf16; ``q_lens``: int32 ``[B]``.
+    """
+    _need(q.is_cuda and q.dim() == 4 and q.shape[3] == ctx.head_dim and q.is_contiguous(),
+          "q must be [B, Lq, Hq, d]")
+    _need(q.dtype in _DTYPES, "q dtype must be fp32/fp16/bf16")
+    B, Lq, Hq, d = q.shape
+    for name, pg, bits in (("k_pages", k_pages, k_bits), ("v_pages", v_pages, v_bits)):
+        _need(pg.dtype == torch.uint8 and pg.dim() == 4 and pg.is_contiguous(), f"{name} must be uint8 4-D")
+        _need(pg.shape[3] == row_bytes(d, bits), f"{name} row_bytes does not match bits")
+    NB, BS, Hkv, _ = k_pages.shape
+    _need(tuple(v_pages.shape[:3]) == (NB, BS, Hkv), "k_pages / v_pages geometry mismatch")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B
+          and block_table.is_contiguous(), "block_table must be int32 [B, max_blocks]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (B,), "seq_lens must be int32 [B]")
+    _need(q_lens.is_cuda and q_lens.dtype == torch.int32 and q_lens.shape == (B,), "q_lens must be int32 [B]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty((B, Lq, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out.dtype == torch.float32 and out.shape == (B, Lq, Hq, d) and out.is_contiguous(),
+          "out must be fp32 [B, Lq, Hq, d]")
+    need = prefill_workspace_bytes(ctx, B, Lq, Hq, Hkv, max_seq_len, BS)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = _lib.lib().tq_paged_prefill(
+        ctx.handle, q.data_ptr(), _DTYPES[q.dtype], B, Lq, q_lens.data_ptr(), Hq, Hkv, k_pages.data_ptr(), k_bits,
+        v_pages.data_ptr(), v_bits, NB, BS, block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(),
+        max_seq_len, float(scale) if scale else 0.0, out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(q))
+    check(st, "tq_paged_prefill")
     return out
 
 

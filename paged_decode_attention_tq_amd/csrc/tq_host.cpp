@@ -817,6 +817,148 @@ tq_status tq_paged_decode_hybrid(const tq_ctx* ctx, const void* q, tq_dtype q_dt
   return hip_status(tq::launch_hybrid(h, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of tq_paged_prefill, in 256-byte aligned pieces: the decode-order
+// queries, the decode-order outputs, prefix and tail lengths, tail slots,
+// the dense tail K and V, then the hybrid decode's workspace for Lq * Hq
+// query heads.
+struct PrefillLayout {
+  size_t vq, vout, plen, tlen, slots, tk, tv, hyb, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool prefill_layout(const tq_ctx* ctx, int batch, int q_len, int num_q_heads, int num_kv_heads, int max_seq_len,
+                    int block_size, size_t q_elem, PrefillLayout* l) {
+  const size_t rows = (size_t)batch * q_len * num_q_heads;
+  const size_t tail = (size_t)batch * (q_len - 1);
+  const size_t hyb = tq_hybrid_workspace_bytes(ctx, batch, num_q_heads * q_len, num_kv_heads, max_seq_len, block_size);
+  if (hyb == 0) return false;
+  size_t off = 0;
+  l->vq = off;
+  off += align256(rows * kHeadDim * q_elem);
+  l->vout = off;
+  off += align256(rows * kHeadDim * sizeof(float));
+  l->plen = off;
+  off += align256((size_t)batch * 4);
+  l->tlen = off;
+  off += align256((size_t)batch * 4);
+  l->slots = off;
+  off += align256(tail * 8);
+  l->tk = off;
+  off += align256(tail * num_kv_heads * kHeadDim * sizeof(float));
+  l->tv = off;
+  off += align256(tail * num_kv_heads * kHeadDim * sizeof(float));
+  l->hyb = off;
+  off += hyb;
+  l->total = off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq_prefill_workspace_bytes(const tq_ctx* ctx, int batch, int q_len, int num_q_heads, int num_kv_heads,
+                                  int max_seq_len, int block_size) {
+  if (batch <= 0 || q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_seq_len < 0) return 0;
+  PrefillLayout l;
+  if (!prefill_layout(ctx, batch, q_len, num_q_heads, num_kv_heads, max_seq_len, block_size, 4, &l)) return 0;
+  return l.total;  // sized for fp32 queries, which covers fp16 / bf16
+}
+
+tq_status tq_paged_prefill(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch, int q_len,
+                           const int32_t* q_lens, int num_q_heads, int num_kv_heads, const uint8_t* k_pages,
+                           int k_bits, const uint8_t* v_pages, int v_bits, int64_t num_blocks, int block_size,
+                           const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                           int max_seq_len, float scale, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!ctx || batch < 0 || q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_seq_len < 0 || block_size <= 0)
+    return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads) return TQ_ERR_INVALID_ARG;
+  if ((long long)(num_q_heads / num_kv_heads) * q_len > tq::kMaxGroup) return TQ_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size < max_seq_len) return TQ_ERR_INVALID_ARG;
+  if (batch == 0) return TQ_OK;
+  if (!q || !q_lens || !seq_lens || !block_table || !out) return TQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(q) & 15) || (reinterpret_cast<uintptr_t>(out) & 15) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return TQ_ERR_ALIGNMENT;
+  PrefillLayout l;
+  if (!prefill_layout(ctx, batch, q_len, num_q_heads, num_kv_heads, max_seq_len, block_size, 4, &l))
+    return TQ_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < l.total) return TQ_ERR_WORKSPACE;
+  if (!bits_ok(k_bits) || !bits_ok(v_bits) || block_size != tq::kBlockSize) return TQ_ERR_UNSUPPORTED;
+  if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const hipStream_t st = (hipStream_t)stream;
+  tq::PrefillArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.q_lens = q_lens;
+  a.seq_lens = seq_lens;
+  a.block_table = block_table;
+  a.vq = ws + l.vq;
+  a.prefix_lens = reinterpret_cast<int32_t*>(ws + l.plen);
+  a.tail_lens = reinterpret_cast<int32_t*>(ws + l.tlen);
+  a.tail_slots = reinterpret_cast<int64_t*>(ws + l.slots);
+  a.vout = reinterpret_cast<float*>(ws + l.vout);
+  a.out = out;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.block_size = block_size;
+  a.max_len = (int)std::min<long long>((long long)max_blocks_per_seq * block_size, 0x7fffffffLL);
+  a.q_dtype = (int)q_dtype;
+  tq_status s = hip_status(tq::launch_prefill_prep(a, st));
+  if (s != TQ_OK) return s;
+  const int tail = q_len - 1;
+  if (tail > 0) {  // the chunk's tokens after the shared prefix, read back densely
+    s = tq_decompress_kv(ctx, k_pages, num_blocks, block_size, num_kv_heads, k_bits, a.tail_slots,
+                         (int64_t)batch * tail, ws + l.tk, TQ_F32, nullptr, stream);
+    if (s != TQ_OK) return s;
+    s = tq_decompress_kv(ctx, v_pages, num_blocks, block_size, num_kv_heads, v_bits, a.tail_slots,
+                         (int64_t)batch * tail, ws + l.tv, TQ_F32, nullptr, stream);
+    if (s != TQ_OK) return s;
+  }
+  const int vheads = num_q_heads * q_len;
+  float* lse = reinterpret_cast<float*>(
+      ws + l.hyb + align256(tq_decode_workspace_bytes(ctx, batch, vheads, num_kv_heads, max_seq_len, block_size)));
+  s = decode_impl(ctx, a.vq, q_dtype, batch, vheads, num_kv_heads, k_pages, k_bits, v_pages, v_bits, num_blocks,
+                  block_size, block_table, max_blocks_per_seq, a.prefix_lens, max_seq_len, scale,
+                  const_cast<float*>(a.vout), lse, ws + l.hyb, l.total - l.hyb, stream);
+  if (s != TQ_OK) return s;
+  if (tail > 0) {
+    tq::HybridArgs h;
+    std::memset(&h, 0, sizeof(h));
+    h.q = a.vq;
+    h.recent_k = ws + l.tk;
+    h.recent_v = ws + l.tv;
+    h.recent_lens = a.tail_lens;
+    h.lse = lse;
+    h.out = const_cast<float*>(a.vout);
+    h.batch = batch;
+    h.num_q_heads = vheads;
+    h.num_kv_heads = num_kv_heads;
+    h.group = vheads / num_kv_heads;
+    h.cap = tail;
+    h.q_dtype = (int)q_dtype;
+    h.r_dtype = (int)TQ_F32;
+    h.causal_group = num_q_heads / num_kv_heads;
+    const float sm_scale = scale > 0 ? scale : 1.0f / std::sqrt((float)kHeadDim);
+    h.scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+    s = hip_status(tq::launch_hybrid(h, st));
+    if (s != TQ_OK) return s;
+  }
+  return hip_status(tq::launch_prefill_out(a, st));
+}
+
 tq_status tq_paged_decode_noalloc(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
                                   int num_q_heads, int num_kv_heads, const uint8_t* k_pages, int k_bits,
                                   const uint8_t* v_pages, int v_bits, int64_t num_blocks, int block_size,

@@ -71,7 +71,10 @@ __device__ __forceinline__ float load1(const void* base, int64_t elem, int dt) {
 //   * softmax and values: the 32 threads of head i (thread = 32 i + dim quad)
 //     update its running maximum and normaliser and 4 output dims over the
 //     64 tokens (online softmax in the log2 domain).
-// Finally the window's part is merged with the packed part's output.
+// Finally the window's part is merged with the packed part's output.  With
+// causal_group set (the chunk tail of a multi-query call), query head h of
+// KV head g is query j = (h - g G) / causal_group of the chunk and sees
+// window rows r < j only.
 template <int RDT>
 __global__ __launch_bounds__(256) void hybrid_window_kernel(HybridArgs a) {
   __shared__ float ks[kChunk * kRow];
@@ -138,8 +141,11 @@ __global__ __launch_bounds__(256) void hybrid_window_kernel(HybridArgs a) {
         s1b = fmaf(q1[2], kv[2], fmaf(q1[3], kv[3], s1b));
       }
       const bool in = c0 + t < R;
-      ps[i0 * kChunk + t] = in ? (s0a + s0b) * a.scale_log2 : -__builtin_inff();
-      ps[i1 * kChunk + t] = in ? (s1a + s1b) * a.scale_log2 : -__builtin_inff();
+      // causal: query j of the chunk (virtual head (j, i)) sees window rows r < j
+      const int lim0 = a.causal_group ? ((h0 - g * G + i0) / a.causal_group) : R;
+      const int lim1 = a.causal_group ? ((h0 - g * G + i1) / a.causal_group) : R;
+      ps[i0 * kChunk + t] = in && c0 + t < lim0 ? (s0a + s0b) * a.scale_log2 : -__builtin_inff();
+      ps[i1 * kChunk + t] = in && c0 + t < lim1 ? (s1a + s1b) * a.scale_log2 : -__builtin_inff();
     }
     __syncthreads();
     if (hi < nh) {
@@ -148,9 +154,11 @@ __global__ __launch_bounds__(256) void hybrid_window_kernel(HybridArgs a) {
       float cm = fmaxf(s0, s1);
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off, 32));
-      const float mn = fmaxf(m, cm);  // finite: the round has at least one token
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf
-      const float p0 = __builtin_amdgcn_exp2f(s0 - mn), p1 = __builtin_amdgcn_exp2f(s1 - mn);
+      const float mn = fmaxf(m, cm);
+      const bool none = mn == -__builtin_inff();  // every token so far masked (causal)
+      const float alpha = none ? 1.0f : __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf
+      const float p0 = none ? 0.0f : __builtin_amdgcn_exp2f(s0 - mn);
+      const float p1 = none ? 0.0f : __builtin_amdgcn_exp2f(s1 - mn);
       float ls = p0 + p1;
 #pragma unroll
       for (int off = 16; off >= 1; off >>= 1) ls += __shfl_xor(ls, off, 32);
@@ -177,9 +185,13 @@ __global__ __launch_bounds__(256) void hybrid_window_kernel(HybridArgs a) {
   const int h = h0 + hi;
   const float lp = a.lse[(int64_t)b * a.num_q_heads + h];
   const float M = fmaxf(lp, m);
-  const float wp = lp == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(lp - M);
-  const float ww = __builtin_amdgcn_exp2f(m - M);
   float* o = a.out + ((int64_t)b * a.num_q_heads + h) * 128 + 4 * dq;
+  if (M == -__builtin_inff()) {  // no token in either part
+    *reinterpret_cast<floatx4*>(o) = floatx4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  const float wp = lp == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(lp - M);
+  const float ww = m == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m - M);
   const floatx4 op = *reinterpret_cast<const floatx4*>(o);
   const float inv = 1.0f / (wp + ww * l);
   *reinterpret_cast<floatx4*>(o) = (wp * op + ww * acc) * inv;

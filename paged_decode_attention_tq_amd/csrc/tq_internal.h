@@ -174,7 +174,34 @@ struct HybridArgs {
   int32_t cap;
   int32_t q_dtype;
   int32_t r_dtype;
+  int32_t causal_group;          // 0, or the query heads per KV head of one query token (causal chunk tail)
   float scale_log2;              // softmax scale * log2(e)
+};
+
+// Arguments of the multi-query (prefill / verify chunk) helpers
+// (tq_prefill.hip).  The chunk's Lq queries of each sequence become Lq * G
+// query heads per KV head of a decode over the prefix every query sees
+// (tokens 0 .. P, P = seq_len - q_len), and the rest of the chunk
+// (tokens P + 1 .. seq_len - 1, read back densely) is a causal window.
+struct PrefillArgs {
+  const void* q;                 // [B, Lq, Hq, 128] of q_dtype
+  const int32_t* q_lens;         // [B], clamped to 0 .. min(Lq, seq_len)
+  const int32_t* seq_lens;       // [B], clamped to 0 .. max_len
+  const int32_t* block_table;    // [B, max_blocks_per_seq]
+  void* vq;                      // [B, Hkv * Lq * G, 128] of q_dtype: query (j, i) of KV head g at g Lq G + j G + i
+  int32_t* prefix_lens;          // [B] P + 1 (0 without queries)
+  int32_t* tail_lens;            // [B] q_len - 1 (0 without queries)
+  int64_t* tail_slots;           // [B, Lq - 1] flat slots of tokens P + 1 + r (-1 past the tail)
+  const float* vout;             // [B, Hkv * Lq * G, 128]
+  float* out;                    // [B, Lq, Hq, 128]
+  int32_t batch;
+  int32_t q_len;                 // Lq
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t block_size;
+  int32_t max_len;
+  int32_t q_dtype;
 };
 
 // Arguments of the split-merge + inverse-rotation kernel.
@@ -209,6 +236,8 @@ int wave_waves(int nh);                           // waves per workgroup (0: not
 hipError_t launch_decode_wave(const WaveArgs& a, int k_bits, int v_bits, int nh, hipStream_t stream);
 hipError_t launch_merge_wave(const WaveMergeArgs& a, hipStream_t stream);
 hipError_t launch_hybrid(const HybridArgs& a, hipStream_t stream);
+hipError_t launch_prefill_prep(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_out(const PrefillArgs& a, hipStream_t stream);
 
 // the static scratch of tq_paged_decode_noalloc (tq_scratch.hip): its size, and
 // its device address on the current device (looked up once per device; nullptr

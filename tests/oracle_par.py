@@ -105,3 +105,25 @@ def sequence_hybrid_outputs(codec, w, b, k_pages, v_pages, queries, recent_k, re
         parts = list(ex.map(job, range(Hkv)))
     return np.concatenate(parts).astype(np.float64)
 
+
+def sequence_prefill_outputs(codec, w, b, k_pages, v_pages, q, q_len):
+    """``oracle.paged_prefill`` outputs ``[Lq, Hq, d]`` of sequence ``b`` from
+    its own pages (identity block table), one KV head (its pages' head slice,
+    its query group) per thread; ``q`` is the sequence's ``[Lq, Hq, d]``."""
+    L = int(w.seq_lens[b])
+    Hq, Hkv = w.num_q_heads, w.num_kv_heads
+    G = Hq // Hkv
+    npg = k_pages.shape[0]
+    bt = np.arange(max(npg, 1), dtype=np.int32)[None]
+    ck, cv = codec.centroids32(w.k_bits), codec.centroids32(w.v_bits)
+
+    def job(g):
+        kp = np.ascontiguousarray(k_pages[:, :, g:g + 1])
+        vp = np.ascontiguousarray(v_pages[:, :, g:g + 1])
+        return oracle.paged_prefill(q[None, :, g * G:(g + 1) * G], np.array([q_len]), kp, vp, bt, np.array([L]),
+                                    w.k_bits, w.v_bits, codec.signs, ck, cv)[0]
+
+    with ThreadPoolExecutor(min(_threads(), Hkv)) as ex:
+        parts = list(ex.map(job, range(Hkv)))
+    return np.concatenate(parts, axis=1).astype(np.float64)
+

@@ -91,6 +91,23 @@ def test_status_strings_and_argument_errors():
     assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, p, p, 1, 16, p, 0.0, p, p, need - 4, None) == 4
     assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, p, p, 1, -1, p, 0.0, p, p, need, None) == 1  # cap < 0
     assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 32, p, 4, p, 64, p, p, 1, 16, p, 0.0, p, p, need, None) == 2  # block 32
+    # multi-query attention
+    pf = lib.tq_paged_prefill
+    a256 = ctypes.c_void_p(256)
+    need = lib.tq_prefill_workspace_bytes(h, 2, 4, 16, 2, 64, 16)
+    assert need > lib.tq_hybrid_workspace_bytes(h, 2, 64, 2, 64, 16)
+    assert pf(h, a256, 1, 2, 9, a256, 16, 2, a256, 4, a256, 4, 8, 16, a256, 4, a256, 64, 0.0, a256, a256, need,
+              None) == 2  # 8 query heads x 9 queries > 64
+    assert pf(h, a256, 1, 2, 0, a256, 16, 2, a256, 4, a256, 4, 8, 16, a256, 4, a256, 64, 0.0, a256, a256, need,
+              None) == 1  # q_len 0
+    assert pf(h, ctypes.c_void_p(260), 1, 2, 4, a256, 16, 2, a256, 4, a256, 4, 8, 16, a256, 4, a256, 64, 0.0, a256,
+              a256, need, None) == 3  # q not 16-byte aligned
+    assert pf(h, a256, 1, 2, 4, a256, 16, 2, a256, 4, a256, 4, 8, 16, a256, 4, a256, 64, 0.0, a256,
+              ctypes.c_void_p(272), need, None) == 3  # workspace not 256-byte aligned
+    assert pf(h, a256, 1, 2, 4, a256, 16, 2, a256, 4, a256, 4, 8, 16, a256, 4, a256, 64, 0.0, a256, a256, need - 1,
+              None) == 4
+    assert pf(h, a256, 1, 2, 4, None, 16, 2, a256, 4, a256, 4, 8, 16, a256, 4, a256, 64, 0.0, a256, a256, need,
+              None) == 1  # no q_lens
     args = dict(batch=2, hq=128, hkv=1)  # group 128 > 64
     assert lib.tq_paged_decode(h, p, 1, 2, 128, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 2
     assert lib.tq_paged_decode(h, p, 1, 2, 6, 4, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, 1 << 20, None) == 1
