@@ -79,3 +79,65 @@ def test_graph_replays_equal_eager(ctx, hkv, G, lens):
         assert torch.equal(out, eager), f"replay {r} differs from the eager call"
         del junk
     assert int(err.item()) == 0
+
+
+def test_graph_readback_hybrid_and_multi_query(ctx):
+    # the other entry points allocate nothing and never synchronise either:
+    # readback + hybrid decode + multi-query attention captured together,
+    # every replay equal to the eager calls bit for bit
+    w = workloads.make_workload("graphx", num_q_heads=16, num_kv_heads=2, seq_lens=[700, 33, 150], seed=44)
+    print(f"[graph] readback + hybrid + multi-query lens={w.seq_lens.tolist()}", flush=True)
+    dev = torch.device("cuda")
+    kp = torch.zeros(w.page_shape(4), dtype=torch.uint8, device=dev)
+    vp = torch.zeros(w.page_shape(4), dtype=torch.uint8, device=dev)
+    slots = torch.from_numpy(w.slots).to(dev)
+    api.write_kv_pair(ctx, torch.from_numpy(w.rows("k")).to(dev), torch.from_numpy(w.rows("v")).to(dev), kp, vp,
+                      slots, 4, 4)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    q = torch.from_numpy(w.queries()).to(dev)
+    rl = np.array([16, 0, 5], dtype=np.int32)
+    rk, rv = w.recent_window(16, rl, seed=3)
+    rk, rv, rl = torch.from_numpy(rk).to(dev), torch.from_numpy(rv).to(dev), torch.from_numpy(rl).to(dev)
+    Lq = 4
+    pq = torch.randn((w.batch, Lq, w.num_q_heads, 128), device=dev).to(torch.float16)
+    ql = torch.tensor([4, 2, 1], dtype=torch.int32, device=dev)
+    dense = torch.empty((w.num_tokens, 2, 128), dtype=torch.float16, device=dev)
+    hout = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=dev)
+    pout = torch.empty((w.batch, Lq, w.num_q_heads, 128), dtype=torch.float32, device=dev)
+    hws = torch.empty(api.hybrid_workspace_bytes(ctx, w.batch, w.num_q_heads, 2, w.max_seq_len), dtype=torch.uint8,
+                      device=dev)
+    pws = torch.empty(api.prefill_workspace_bytes(ctx, w.batch, Lq, w.num_q_heads, 2, w.max_seq_len),
+                      dtype=torch.uint8, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        api.decompress_kv(ctx, kp, slots, 4, out=dense, err_count=err, check_slots=False)
+        api.paged_decode_hybrid(ctx, q, kp, vp, bt, lens, rk, rv, rl, 4, 4, max_seq_len=w.max_seq_len, out=hout,
+                                workspace=hws)
+        api.paged_prefill(ctx, pq, ql, kp, vp, bt, lens, 4, 4, max_seq_len=w.max_seq_len, out=pout, workspace=pws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [dense.clone(), hout.clone(), pout.clone()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in (dense, hout, pout):
+            t.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((dense, hout, pout), eager):
+            assert torch.equal(got, want), f"replay {r} differs from the eager call"
+        del junk
+    assert int(err.item()) == 0
