@@ -44,6 +44,15 @@ from .codec import (
     OracleCodec,
 )
 from .attention import paged_decode, paged_decode_heads, paged_decode_hybrid, paged_prefill
+from .qjl import (
+    prod_row_bytes,
+    encode_prod,
+    prod_rows_to_bytes,
+    prod_bytes_to_rows,
+    prod_scores,
+    write_prod,
+    paged_prod_scores,
+)
 
 __all__ = [
     "beta_codebook",
@@ -69,4 +78,11 @@ __all__ = [
     "paged_decode_heads",
     "paged_decode_hybrid",
     "paged_prefill",
+    "prod_row_bytes",
+    "encode_prod",
+    "prod_rows_to_bytes",
+    "prod_bytes_to_rows",
+    "prod_scores",
+    "write_prod",
+    "paged_prod_scores",
 ]

@@ -26,7 +26,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-__all__ = ["Workload", "make_workload", "PRESETS", "preset", "random_pages"]
+__all__ = ["Workload", "make_workload", "PRESETS", "preset", "random_pages", "qjl_matrix"]
 
 
 def _rng(seed, *key):
@@ -265,4 +265,11 @@ def random_pages(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: 
     idx = g.integers(0, 256, size=shape + (ib,), dtype=np.uint8)
     norm = (math.sqrt(head_dim) * g.lognormal(0.0, 0.5, size=shape)).astype("<f4")
     return np.concatenate([idx, norm[..., None].view(np.uint8)], axis=-1)
+
+
+def qjl_matrix(d: int = 128, seed: int = 0) -> np.ndarray:
+    """A ``d x d`` float32 matrix of i.i.d. N(0, 1) entries (stream ``(7,)`` of
+    ``seed``): the sketch matrix of the prod key codec, an input of both the
+    GPU path and the oracle."""
+    return _rng(seed, 7).standard_normal((d, d), dtype=np.float32)
 
