@@ -101,15 +101,20 @@ def prod_bytes_to_rows(rows, bits: int, d: int):
 
 
 def prod_scores(y, rows, bits: int, signs, S):
-    """Estimated inner products of query ``y[d]`` with each row of ``rows[..., RB]`` (float64)."""
+    """Estimated inner products of query ``y[d]`` (or of each query of
+    ``y[m, d]``) with each row of ``rows[..., RB]`` (float64; shape
+    ``rows.shape[:-1]``, or ``(m,) + rows.shape[:-1]``)."""
     d = len(signs)
     idx, norm, z, gamma = prod_bytes_to_rows(rows, bits, d)
     _, c32, _ = beta_codebook(d, bits - 1)
-    yr = rht(np.asarray(y, dtype=np.float64), signs)
-    sy = np.asarray(S, dtype=np.float64) @ yr
-    mse = c32.astype(np.float64)[idx.astype(np.int64)] @ yr
-    qjl = np.where(z, 1.0, -1.0) @ sy
-    return norm.astype(np.float64) * (mse + gamma.astype(np.float64) * np.sqrt(np.pi / 2.0) / d * qjl)
+    y = np.asarray(y, dtype=np.float64)
+    yr = rht(np.atleast_2d(y), signs)                 # y~ per query, [m, d]
+    sy = yr @ np.asarray(S, dtype=np.float64).T       # S y~ per query
+    mse = c32.astype(np.float64)[idx.astype(np.int64)] @ yr.T   # [..., m]
+    qjl = np.where(z, 1.0, -1.0) @ sy.T
+    est = norm.astype(np.float64)[..., None] * (mse + gamma.astype(np.float64)[..., None] * np.sqrt(np.pi / 2.0) / d * qjl)
+    est = np.moveaxis(est, -1, 0)
+    return est[0] if y.ndim == 1 else est
 
 
 def write_prod(raw, pages, slots, bits: int, signs, S):
@@ -152,9 +157,10 @@ def paged_prod_scores(q, pages, block_table, seq_lens, bits: int, signs, S):
     out = np.zeros((B, Hq, Lmax))
     for b in range(B):
         L = int(seq_lens[b])
+        if L == 0:
+            continue
         t = np.arange(L)
         blk = np.asarray(block_table[b])[t // BS]
-        for h in range(Hq):
-            if L:
-                out[b, h, :L] = prod_scores(q[b, h], pages[blk, t % BS, h // G], bits, signs, S)
+        for g in range(Hkv):
+            out[b, g * G:(g + 1) * G, :L] = prod_scores(q[b, g * G:(g + 1) * G], pages[blk, t % BS, g], bits, signs, S)
     return out
