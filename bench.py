@@ -237,6 +237,76 @@ def bench_decompress(args, torch, api, w, ctx, kp, slots):
     return result
 
 
+def bench_prod(args, torch, api, w, ctx, kraw_d, slots, q):
+    """The prod key codec on the workload's K rows: the writer over every row,
+    then the inner-product scores of every query head over every key, timed
+    with events (each after the cache flush)."""
+    from paged_decode_attention_tq_amd import workloads
+
+    dev = kraw_d.device
+    bits = w.k_bits
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    RB = api.prod_row_bytes(d, bits)
+    pages = torch.zeros((w.num_blocks, 16, Hkv, RB), dtype=torch.uint8, device=dev)
+    S = torch.from_numpy(workloads.qjl_matrix(d, seed=0)).to(dev)
+    q_d = torch.from_numpy(q).to(dev)
+    bt, lens = torch.from_numpy(w.block_table).to(dev), torch.from_numpy(w.seq_lens).to(dev)
+    scores = torch.empty((B, Hq, w.max_seq_len), dtype=torch.float32, device=dev)
+    ws = torch.empty(2 * B * Hq * d * 4, dtype=torch.uint8, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_rd = None if args.no_flush else torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def call(i=None):
+        for k, fn in enumerate((
+                lambda: api.write_kv_prod(ctx, kraw_d, pages, slots, bits, S, err_count=err, check_slots=False),
+                lambda: api.prod_scores(ctx, q_d, pages, bt, lens, bits, S, max_seq_len=w.max_seq_len, out=scores,
+                                        workspace=ws))):
+            if flush is not None:
+                flush.zero_()
+                flush_rd.sum()
+            if i is not None:
+                ev[i][2 * k].record()
+            fn()
+            if i is not None:
+                ev[i][2 * k + 1].record()
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        call(i)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    wms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    sms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    rows = kraw_d.shape[0] * Hkv
+    kept = int((w.slots >= 0).sum()) * Hkv
+    wbytes = kraw_d.numel() * kraw_d.element_size() + kept * RB
+    sbytes = w.num_tokens * Hkv * RB + B * Hq * w.max_seq_len * 4
+    log(f"[bench] prod writer ms: mean {wms.mean():.4f}; scores ms: mean {sms.mean():.4f}")
+    ssec = float(sms.mean()) / 1e3
+    return {
+        "metric": "TQ prod key codec: scores (key-query inner products)/s + HBM GB/s (% of peak), 1 MI355X",
+        "value": Hq * w.num_tokens / ssec,
+        "unit": "scores/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": float(sms.mean()),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"u8 prod rows ({bits - 1}-bit indices + 1-bit sketch), fp32 arithmetic",
+        "data": "synthetic (the workload's K rows; a seeded Gaussian sketch matrix)",
+        "config": {"workload": f"{w.name} K rows as {bits}-bit prod rows: {w.num_tokens} tokens x Hkv {Hkv}, "
+                               f"Hq {Hq}, head_dim {d}, block 16"},
+        "scores_ms": float(sms.mean()), "scores_ms_min": float(sms.min()),
+        "writer_ms": float(wms.mean()), "writer_rows_per_s": rows / (float(wms.mean()) / 1e3),
+        "writer_gbps": wbytes / (float(wms.mean()) / 1e3) / 1e9,
+        "roofline": {"bound": "hbm", "kernel": "tq_prod_scores (prod_query_kernel + prod_scores_kernel)",
+                     "achieved": sbytes / ssec / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": sbytes / ssec / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": sbytes, "traffic": None},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,10 +317,11 @@ def main():
     ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush (1 GiB write, then 1 GiB read) before each timed step")
-    ap.add_argument("--op", choices=("decode", "decompress", "hybrid", "prefill"), default="decode",
+    ap.add_argument("--op", choices=("decode", "decompress", "hybrid", "prefill", "prod"), default="decode",
                     help="decode: the decode step (default); decompress: the dense readback of every K row; "
                          "hybrid: the decode step over the packed pages plus an exact fp16 window per sequence; "
-                         "prefill: a chunk of --q-len queries per sequence attending causally over the pages")
+                         "prefill: a chunk of --q-len queries per sequence attending causally over the pages; "
+                         "prod: the prod key codec (writer of every K row, then every head's scores over them)")
     ap.add_argument("--q-len", type=int, default=8, help="queries per sequence (--op prefill)")
     ap.add_argument("--window", type=int, default=128, help="recent-window rows per sequence (--op hybrid)")
     ap.add_argument("--out-dtype", choices=("fp16", "bf16", "fp32"), default="fp16",
@@ -306,6 +377,10 @@ def main():
     log(f"[bench] pages written (prefill): {write['rows']} rows in {write['ms']:.3f} ms, "
         f"{write['rows_per_s'] / 1e6:.1f} M rows/s, {write['gbps']:.0f} GB/s")
 
+    if args.op == "prod":
+        del vraw_d
+        print(json.dumps(bench_prod(args, torch, api, w, ctx, kraw_d, slots, q)), flush=True)
+        return
     if args.op == "decompress":
         del kraw_d, vraw_d
         print(json.dumps(bench_decompress(args, torch, api, w, ctx, kp, slots)), flush=True)

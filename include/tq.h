@@ -164,6 +164,55 @@ tq_status tq_decompress_kv(const tq_ctx* ctx, const uint8_t* pages, int64_t num_
                            int num_kv_heads, int bits, const int64_t* slots, int64_t num_tokens,
                            void* out, tq_dtype out_dtype, int32_t* err_count, void* stream);
 
+/* Inner-product ("prod") key rows: the published TurboQuant inner-product
+ * quantiser, which the pages name ("vLLM Reference Audit", File Map row "MSE
+ * and QJL codecs": TurboQuantProd, indices, norms, signs; Feature Checklist
+ * row "QJL residual") without its arithmetic or layout.  A b-bit row encodes
+ * the rotated unit vector r with the (b-1)-bit codec of the MSE rows, then
+ * sketches its residual e = r - c[idx] with a d x d matrix S of N(0, 1)
+ * entries: z_i = +1 when (S e)_i >= 0, and gamma = ||e||.  Layout (this
+ * library's): ceil(d (b-1) / 8) index bytes, fp32 norm, d / 8 sign bytes
+ * (bit i = z_i > 0, LSB-first), fp32 gamma; 40/56/72/88 bytes at d = 128
+ * for b = 2..5.  Returns 0 for a head_dim not a multiple of 8 or bits
+ * outside 2..8. */
+size_t tq_prod_row_bytes(int head_dim, int bits);
+
+/* Write prod key rows (as tq_write_kv: same raw rows, slots, page shape with
+ * tq_prod_row_bytes rows, errors and err_count).  sketch: device fp32
+ * [head_dim, head_dim] row-major, 16-byte aligned: the matrix S, an input
+ * (the method's random draw).  gamma is computed in fp32 from the fp32
+ * residual; the sign of a projection within fp32 rounding of zero may differ
+ * from an exact computation.  bits 2..5.  Asynchronous, allocates nothing. */
+tq_status tq_write_kv_prod(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype,
+                           int64_t num_tokens, int num_kv_heads, uint8_t* pages,
+                           int64_t num_blocks, int block_size, const int64_t* slots,
+                           int bits, const float* sketch, int32_t* err_count, void* stream);
+
+/* Bytes of device workspace tq_prod_scores needs: two rows of 128 floats per
+ * query head.  0 for a non-positive batch or head count. */
+size_t tq_prod_scores_workspace_bytes(int batch, int num_q_heads);
+
+/* Estimated inner products of every query head with every key of its
+ * sequence over prod key pages (the score-only diagnostic the pages list as
+ * the packed score kernel, "vLLM Reference Audit", File Map): for token t of
+ * sequence b and query head h (KV head h / (num_q_heads / num_kv_heads)),
+ * scores[b, h, t] = n (<q~, c[idx]> + gamma sqrt(pi / 2) / d <S q~, z>) with
+ * q~ = rht(q): unbiased for <q, k> over the draw of S.
+ *   q, block_table, seq_lens, max_seq_len: as tq_paged_decode.
+ *   pages       device, prod rows [num_blocks, 16, num_kv_heads,
+ *               tq_prod_row_bytes(head_dim, bits)], 4-byte aligned.
+ *   sketch      the writer's S.
+ *   scores      device, fp32 [batch, num_q_heads, max_seq_len]; entries past a
+ *               sequence's length are written as 0.
+ *   workspace   device, >= tq_prod_scores_workspace_bytes(...), 16-byte aligned.
+ * Asynchronous, allocates nothing; errors as tq_paged_decode. */
+tq_status tq_prod_scores(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
+                         int num_q_heads, int num_kv_heads, const uint8_t* pages, int bits,
+                         int64_t num_blocks, int block_size, const int32_t* block_table,
+                         int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len,
+                         const float* sketch, float* scores, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Bytes of device workspace tq_paged_decode needs for these sizes (the
  * split partials: a normalised rotated sum and a log-sum-exp per query head
  * and split).  The count of splits follows the current device's compute

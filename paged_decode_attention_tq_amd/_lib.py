@@ -44,6 +44,19 @@ SIGNATURES = {
         [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int,
          _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p],
     ),
+    "tq_prod_row_bytes": (_c.c_size_t, [_c.c_int, _c.c_int]),
+    "tq_write_kv_prod": (
+        _c.c_int,
+        [_c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int64,
+         _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p],
+    ),
+    "tq_prod_scores_workspace_bytes": (_c.c_size_t, [_c.c_int, _c.c_int]),
+    "tq_prod_scores": (
+        _c.c_int,
+        [_c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_int,
+         _c.c_int64, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_void_p,
+         _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p],
+    ),
     "tq_decompress_kv": (
         _c.c_int,
         [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int, _c.c_int, _c.c_int, _c.c_void_p, _c.c_int64,

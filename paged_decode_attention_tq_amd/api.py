@@ -22,6 +22,9 @@ __all__ = [
     "Context",
     "write_kv",
     "write_kv_pair",
+    "prod_row_bytes",
+    "write_kv_prod",
+    "prod_scores",
     "decompress_kv",
     "decode_workspace_bytes",
     "decode_kernel",
@@ -152,6 +155,73 @@ def write_kv_pair(ctx: Context, raw_k: torch.Tensor, raw_v: torch.Tensor, k_page
             raise TQError(f"tq_write_kv_pair: {n_bad} slot(s) outside the allocated pages")
         return n_bad
     return 0
+
+
+def prod_row_bytes(head_dim: int, bits: int) -> int:
+    return int(_lib.lib().tq_prod_row_bytes(head_dim, bits))
+
+
+def write_kv_prod(ctx: Context, raw: torch.Tensor, pages: torch.Tensor, slots: torch.Tensor, bits: int,
+                  sketch: torch.Tensor, err_count: torch.Tensor | None = None, check_slots: bool = True) -> int:
+    """Encode ``raw[N, Hkv, d]`` into prod key rows of ``pages[NB, BS, Hkv, RB]`` at
+    ``slots[N]`` with the sketch matrix ``sketch`` (fp32 ``[d, d]``).  Slot rules as ``write_kv``."""
+    _need(raw.is_cuda and pages.is_cuda and slots.is_cuda and sketch.is_cuda, "tensors must be on the GPU")
+    _need(raw.dim() == 3 and raw.shape[2] == ctx.head_dim and raw.is_contiguous(), "raw must be [N, Hkv, d]")
+    _need(pages.dtype == torch.uint8 and pages.dim() == 4 and pages.is_contiguous(), "pages must be uint8 4-D")
+    NB, BS, Hkv, RB = pages.shape
+    _need(raw.shape[1] == Hkv, "num_kv_heads mismatch")
+    _need(RB == prod_row_bytes(ctx.head_dim, bits), "pages row_bytes does not match bits")
+    _need(slots.dtype == torch.int64 and slots.shape == (raw.shape[0],) and slots.is_contiguous(),
+          "slots must be int64 [N]")
+    _need(raw.dtype in _DTYPES, "raw dtype must be fp32/fp16/bf16")
+    _need(sketch.dtype == torch.float32 and sketch.shape == (ctx.head_dim, ctx.head_dim) and sketch.is_contiguous(),
+          "sketch must be fp32 [d, d]")
+    own = err_count is None and check_slots
+    if own:
+        err_count = torch.zeros(1, dtype=torch.int32, device=raw.device)
+    st = _lib.lib().tq_write_kv_prod(
+        ctx.handle, raw.data_ptr(), _DTYPES[raw.dtype], raw.shape[0], Hkv, pages.data_ptr(), NB, BS,
+        slots.data_ptr(), bits, sketch.data_ptr(), err_count.data_ptr() if err_count is not None else None,
+        _stream(raw))
+    check(st, "tq_write_kv_prod")
+    if check_slots:
+        n_bad = int(err_count.item())
+        if n_bad:
+            raise TQError(f"tq_write_kv_prod: {n_bad} slot(s) outside the allocated pages")
+        return n_bad
+    return 0
+
+
+def prod_scores(ctx: Context, q: torch.Tensor, pages: torch.Tensor, block_table: torch.Tensor,
+                seq_lens: torch.Tensor, bits: int, sketch: torch.Tensor, max_seq_len: int | None = None,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Estimated ``<q[b, h], k_t>`` over prod key pages -> fp32 ``[B, Hq, max_seq_len]``."""
+    _need(q.is_cuda and q.dim() == 3 and q.shape[2] == ctx.head_dim and q.is_contiguous(), "q must be [B, Hq, d]")
+    _need(q.dtype in _DTYPES, "q dtype must be fp32/fp16/bf16")
+    B, Hq, d = q.shape
+    _need(pages.dtype == torch.uint8 and pages.dim() == 4 and pages.is_contiguous(), "pages must be uint8 4-D")
+    NB, BS, Hkv, RB = pages.shape
+    _need(RB == prod_row_bytes(d, bits), "pages row_bytes does not match bits")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B
+          and block_table.is_contiguous(), "block_table must be int32 [B, max_blocks]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (B,), "seq_lens must be int32 [B]")
+    _need(sketch.dtype == torch.float32 and sketch.shape == (d, d) and sketch.is_contiguous(),
+          "sketch must be fp32 [d, d]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty((B, Hq, max_seq_len), dtype=torch.float32, device=q.device)
+    _need(out.dtype == torch.float32 and out.shape == (B, Hq, max_seq_len) and out.is_contiguous(),
+          "out must be fp32 [B, Hq, max_seq_len]")
+    need = int(_lib.lib().tq_prod_scores_workspace_bytes(B, Hq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = _lib.lib().tq_prod_scores(
+        ctx.handle, q.data_ptr(), _DTYPES[q.dtype], B, Hq, Hkv, pages.data_ptr(), bits, NB, BS,
+        block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(), max_seq_len, sketch.data_ptr(),
+        out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
+    check(st, "tq_prod_scores")
+    return out
 
 
 def decompress_kv(ctx: Context, pages: torch.Tensor, slots: torch.Tensor, bits: int,

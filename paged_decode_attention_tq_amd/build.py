@@ -6,7 +6,8 @@ Compiles ``csrc/tq_host.cpp`` (host C++: the C ABI, context, codebook
 solver), ``csrc/tq_write.hip`` (row writer), ``csrc/tq_decompress.hip``
 (dense readback of rows), ``csrc/tq_hybrid.hip`` (recent-window part of
 the hybrid decode), ``csrc/tq_prefill.hip`` (layout kernels of the
-multi-query attention), ``csrc/tq_decode.hip`` (staged
+multi-query attention), ``csrc/tq_qjl.hip`` (inner-product scores over prod
+key rows), ``csrc/tq_decode.hip`` (staged
 paged decode and merge) and ``csrc/tq_decode_wave.hip`` (wave-private paged
 decode and merge) and ``csrc/tq_scratch.hip`` (the static scratch of the
 allocation-free decode) for gfx950 with hipcc into
@@ -44,7 +45,7 @@ HIP_FLAGS = [
 # per-source extras: the decode never produces NaNs on valid input, so it
 # drops IEEE NaN quieting (fmaxf then needs no canonicalisation)
 SOURCES = ("tq_host.cpp", "tq_write.hip", "tq_decompress.hip", "tq_decode.hip", "tq_decode_wave.hip",
-           "tq_hybrid.hip", "tq_prefill.hip", "tq_scratch.hip")
+           "tq_hybrid.hip", "tq_prefill.hip", "tq_qjl.hip", "tq_scratch.hip")
 
 EXTRA_FLAGS = {
     "tq_decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],

@@ -552,6 +552,87 @@ tq_status tq_decompress_kv(const tq_ctx* ctx, const uint8_t* pages, int64_t num_
   return hip_status(tq::launch_decompress(a, bits, (int)out_dtype, device_cu_count(), (hipStream_t)stream));
 }
 
+size_t tq_prod_row_bytes(int head_dim, int bits) {
+  if (head_dim <= 0 || head_dim % 8 || bits < 2 || bits > 8) return 0;
+  return ((size_t)head_dim * (bits - 1) + 7) / 8 + 4 + (size_t)head_dim / 8 + 4;
+}
+
+tq_status tq_write_kv_prod(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype, int64_t num_tokens,
+                           int num_kv_heads, uint8_t* pages, int64_t num_blocks, int block_size,
+                           const int64_t* slots, int bits, const float* sketch, int32_t* err_count, void* stream) {
+  if (!bits_ok(bits)) return TQ_ERR_UNSUPPORTED;
+  tq::ProdWriteArgs a;
+  std::memset(&a, 0, sizeof(a));
+  // the MSE part: the (bits - 1)-bit codec's boundaries; 1-bit indices are
+  // the sign of each coordinate
+  const tq_status st = make_write_args(ctx, raw, raw_dtype, num_tokens, num_kv_heads, pages, num_blocks, block_size,
+                                       slots, bits == 2 ? 2 : bits - 1, err_count, &a.w);
+  if (st != TQ_OK || num_tokens == 0) return st;
+  if (!sketch) return TQ_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(sketch) & 15) return TQ_ERR_ALIGNMENT;
+  const int mb = bits - 1, n = 1 << mb;
+  a.w.row_bytes = (int)tq_prod_row_bytes(kHeadDim, bits);
+  a.w.page_bytes = (int64_t)block_size * num_kv_heads * a.w.row_bytes;
+  std::memset(a.w.pos_bounds, 0, sizeof(a.w.pos_bounds));
+  for (int j = 0; j < n / 2 - 1; ++j) a.w.pos_bounds[j] = ctx->bound[mb][n / 2 + j];
+  for (int j = 0; j < n / 2; ++j) a.cpos[j] = ctx->cent[mb][n / 2 + j];
+  a.sketch = sketch;
+  if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
+  return hip_status(tq::launch_write_prod(a, (int)raw_dtype, bits, device_cu_count(), (hipStream_t)stream));
+}
+
+size_t tq_prod_scores_workspace_bytes(int batch, int num_q_heads) {
+  if (batch <= 0 || num_q_heads <= 0) return 0;
+  return 2 * (size_t)batch * num_q_heads * kHeadDim * sizeof(float);
+}
+
+tq_status tq_prod_scores(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch, int num_q_heads,
+                         int num_kv_heads, const uint8_t* pages, int bits, int64_t num_blocks, int block_size,
+                         const int32_t* block_table, int max_blocks_per_seq, const int32_t* seq_lens,
+                         int max_seq_len, const float* sketch, float* scores, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!ctx || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      max_seq_len < 0)
+    return TQ_ERR_INVALID_ARG;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_F16 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads) return TQ_ERR_INVALID_ARG;
+  if (!bits_ok(bits) || block_size != tq::kBlockSize) return TQ_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * block_size < max_seq_len) return TQ_ERR_INVALID_ARG;
+  if (batch == 0) return TQ_OK;
+  if (!q || !pages || !block_table || !seq_lens || !sketch || !scores) return TQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(pages) & 3) || (reinterpret_cast<uintptr_t>(sketch) & 15) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 15) || (reinterpret_cast<uintptr_t>(q) & 3) ||
+      (reinterpret_cast<uintptr_t>(scores) & 3))
+    return TQ_ERR_ALIGNMENT;
+  if (!workspace || workspace_bytes < tq_prod_scores_workspace_bytes(batch, num_q_heads)) return TQ_ERR_WORKSPACE;
+  const int row_bytes = (int)tq_prod_row_bytes(kHeadDim, bits);
+  if ((long long)block_size * num_kv_heads * row_bytes > (1 << 30)) return TQ_ERR_UNSUPPORTED;
+  if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
+  tq::ProdScoreArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.pages = pages;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.sketch = sketch;
+  a.qr = static_cast<float*>(workspace);
+  a.sq = a.qr + (size_t)batch * num_q_heads * kHeadDim;
+  a.scores = scores;
+  a.page_bytes = (int64_t)block_size * num_kv_heads * row_bytes;
+  a.num_blocks = num_blocks;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_seq_len = max_seq_len;
+  a.max_len = (int)std::min<long long>((long long)max_blocks_per_seq * block_size, 0x7fffffffLL);
+  a.row_bytes = row_bytes;
+  a.q_dtype = (int)q_dtype;
+  std::memcpy(a.sign_bits, ctx->sign_bits, sizeof(a.sign_bits));
+  std::memcpy(a.cent, ctx->cent[bits - 1], sizeof(float) << (bits - 1));
+  return hip_status(tq::launch_prod_scores(a, bits, (hipStream_t)stream));
+}
+
 size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads, int num_kv_heads,
                                  int max_seq_len, int block_size) {
   (void)ctx;

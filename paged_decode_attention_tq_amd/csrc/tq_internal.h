@@ -28,6 +28,41 @@ struct WriteArgs {
   float pos_bounds[16];     // the 2^(b-1) - 1 positive boundaries, increasing
 };
 
+// Arguments of the prod key writer (tq_write.hip): the MSE part of w uses
+// bits - 1 (pos_bounds are that codebook's), sketch is the d x d matrix S
+// (row-major fp32, device), cpos the 2^(bits-2) positive centroids of the
+// bits - 1 codebook, increasing.
+struct ProdWriteArgs {
+  WriteArgs w;
+  const float* sketch;
+  float cpos[16];
+};
+
+// Arguments of the prod-key score kernels (tq_qjl.hip): estimated inner
+// products of each query head with every key row of its sequence.
+struct ProdScoreArgs {
+  const void* q;                 // [B, Hq, 128] of q_dtype
+  const uint8_t* pages;          // prod rows [num_blocks, 16, Hkv, row_bytes]
+  const int32_t* block_table;    // [B, max_blocks_per_seq]
+  const int32_t* seq_lens;       // [B], clamped to 0 .. max_len
+  const float* sketch;           // [128, 128] row-major
+  float* qr;                     // [B, Hq, 128] workspace: rht(q)
+  float* sq;                     // [B, Hq, 128] workspace: S rht(q)
+  float* scores;                 // [B, Hq, max_seq_len]
+  int64_t page_bytes;
+  int64_t num_blocks;            // block ids outside [0, num_blocks) read as zero rows
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t max_seq_len;           // columns of scores
+  int32_t max_len;               // lengths are clamped to this (the block table's reach)
+  int32_t row_bytes;
+  int32_t q_dtype;
+  uint32_t sign_bits[kHeadDim / 32];
+  float cent[16];                // the 2^(bits-1) centroids of the index codebook
+};
+
 // Arguments of the dense readback kernel (tq_decompress.hip).
 struct ReadArgs {
   const uint8_t* pages;     // [num_blocks, block_size, num_kv_heads, row_bytes]
@@ -221,6 +256,9 @@ struct MergeArgs {
 };
 
 hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t stream);
+// prod key rows of `bits` bits (2..5): indices at bits - 1, sketch signs, gamma
+hipError_t launch_write_prod(const ProdWriteArgs& a, int raw_dtype, int bits, int num_cus, hipStream_t stream);
+hipError_t launch_prod_scores(const ProdScoreArgs& a, int bits, hipStream_t stream);
 // K and V rows of the same tokens (same num_rows) in one launch
 hipError_t launch_write_pair(const WriteArgs& k, const WriteArgs& v, int raw_dtype, int k_bits, int v_bits,
                              hipStream_t stream);

@@ -127,3 +127,26 @@ def sequence_prefill_outputs(codec, w, b, k_pages, v_pages, q, q_len):
         parts = list(ex.map(job, range(Hkv)))
     return np.concatenate(parts, axis=1).astype(np.float64)
 
+
+def sequence_prod_pages(w, b, bits, signs, S):
+    """The oracle's prod key pages of sequence ``b`` (identity block table), as
+    ``sequence_pages``: ``(pages, near_idx, near_sign, kept_tokens)``."""
+    L = int(w.seq_lens[b])
+    bs = w.block_size
+    raw = w.seq_rows("k", b)
+    lo = int(w.cu_seqlens[b])
+    dropped = w.slots[lo:lo + L] < 0
+
+    def job(c0):
+        c1 = min(L, c0 + CHUNK_TOKENS)
+        n = c1 - c0
+        npg = (n + bs - 1) // bs
+        slots = np.where(dropped[c0:c1], -1, np.arange(n)).astype(np.int64)
+        zero = np.zeros((npg, bs, w.num_kv_heads, oracle.prod_row_bytes(w.head_dim, bits)), dtype=np.uint8)
+        return oracle.write_prod(raw[c0:c1], zero, slots, bits, signs, S)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        parts = list(ex.map(job, range(0, L, CHUNK_TOKENS)))
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
+            np.concatenate([p[2] for p in parts]), int((~dropped).sum()))
+

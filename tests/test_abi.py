@@ -91,6 +91,21 @@ def test_status_strings_and_argument_errors():
     assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, p, p, 1, 16, p, 0.0, p, p, need - 4, None) == 4
     assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, p, p, 1, -1, p, 0.0, p, p, need, None) == 1  # cap < 0
     assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 32, p, 4, p, 64, p, p, 1, 16, p, 0.0, p, p, need, None) == 2  # block 32
+    # the prod key codec
+    assert [lib.tq_prod_row_bytes(128, b) for b in (2, 3, 4, 5)] == [40, 56, 72, 88]
+    assert lib.tq_prod_row_bytes(128, 1) == 0 and lib.tq_prod_row_bytes(100, 4) == 0
+    wp = lib.tq_write_kv_prod
+    assert wp(h, a64, 1, 4, 2, a64, 4, 16, a64, 6, a64, None, None) == 2  # bits 6
+    assert wp(h, a64, 1, 4, 2, a64, 4, 16, a64, 4, None, None, None) == 1  # no sketch
+    assert wp(h, a64, 1, 4, 2, a64, 4, 16, a64, 4, ctypes.c_void_p(68), None, None) == 3  # sketch alignment
+    assert wp(h, a64, 1, 0, 2, a64, 4, 16, a64, 4, None, None, None) == 0  # nothing to write
+    ps = lib.tq_prod_scores
+    wsb = lib.tq_prod_scores_workspace_bytes(2, 8)
+    assert wsb == 2 * 2 * 8 * 128 * 4
+    assert ps(h, a64, 1, 2, 8, 2, a64, 4, 8, 16, a64, 4, a64, 64, a64, a64, a64, wsb - 4, None) == 4
+    assert ps(h, a64, 1, 2, 8, 2, a64, 7, 8, 16, a64, 4, a64, 64, a64, a64, a64, wsb, None) == 2  # bits 7
+    assert ps(h, a64, 1, 2, 8, 2, a64, 4, 8, 16, a64, 4, a64, 64, None, a64, a64, wsb, None) == 1  # no sketch
+    assert ps(h, a64, 1, 2, 8, 3, a64, 4, 8, 16, a64, 4, a64, 64, a64, a64, a64, wsb, None) == 1  # 8 % 3
     # multi-query attention
     pf = lib.tq_paged_prefill
     a256 = ctypes.c_void_p(256)

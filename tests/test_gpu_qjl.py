@@ -1,0 +1,154 @@
+"""GPU parity of the prod key codec (tq_write_kv_prod) and its inner-product
+scores (tq_prod_scores) against the oracle.
+
+Writer: every stored row compared field by field with the oracle's encoding
+of the same raw rows under the same sketch matrix: indices equal except at
+near-boundary coordinates (as the MSE rows, and such rows are fewer than
+1e-4 of all indices), norm bytes equal; on rows whose indices all match, the
+sign bits equal except where the projection lies within fp32 rounding of
+zero (marked by the oracle), and gamma (fp32 arithmetic on the GPU) within
+2e-6 relative.
+
+Scores: the GPU's estimate against the oracle's estimator over the same
+page bytes, |d| <= 1e-5 * (|ref| + n * ||q||) per score (sums of 128
+products in fp32); rel-L2 printed.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_decode_attention_tq_amd import api, workloads
+from tests.oracle_par import sequence_prod_pages
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    return api.Context(128, 42)
+
+
+def _compare_rows(got, ref, near_i, near_s, bits, what):
+    """got / ref: prod row bytes [..., RB]; near masks [..., d].  Returns counts."""
+    d = 128
+    gi, gn, gz, gg = oracle.prod_bytes_to_rows(got, bits, d)
+    ri, rn, rz, rg = oracle.prod_bytes_to_rows(ref, bits, d)
+    assert np.array_equal(gn.view(np.uint32), rn.view(np.uint32)), f"{what}: norm bytes differ"
+    bad_i = gi != ri
+    assert not (bad_i & ~near_i).any(), f"{what}: index mismatch away from a boundary"
+    frac = bad_i.sum() / max(1, bad_i.size)
+    assert frac < 1e-4, f"{what}: {bad_i.sum()} near-boundary index mismatches ({frac:.2e})"
+    same = ~bad_i.any(axis=-1)
+    bad_z = (gz != rz) & same[..., None]
+    assert not (bad_z & ~near_s).any(), f"{what}: sign mismatch away from zero"
+    np.testing.assert_allclose(gg[same], rg[same], rtol=2e-6, atol=1e-9, err_msg=f"{what}: gamma")
+    print(f"  {what}: {int(bad_i.sum())} near-boundary index, {int(bad_z.sum())} near-zero sign mismatches "
+          f"over {bad_i.size} coordinates", flush=True)
+
+
+def _check_scores(got, ref, q, norms, what):
+    tol = 1e-5 * (np.abs(ref) + norms * np.linalg.norm(q.astype(np.float64), axis=-1)[..., None])
+    d = np.abs(got.astype(np.float64) - ref)
+    assert (d <= tol).all(), f"{what}: worst excess {float((d - tol).max()):.3e}"
+    rel = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    print(f"  {what}: max|d| {d.max():.3e} relL2 {rel:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_writer_matches_oracle(ctx, bits, dt):
+    w = workloads.make_workload(f"qjl{bits}", num_q_heads=8, num_kv_heads=2, seq_lens=[300, 45, 129],
+                                seed=110 + bits, drop_frac=0.1, lognormal_sigma=0.5, dtype=dt)
+    print(f"[qjl] writer bits={bits} dtype={np.dtype(dt).name} N={w.num_tokens}", flush=True)
+    S = workloads.qjl_matrix(128, seed=bits)
+    signs = oracle.rht_signs(42, 128)
+    shape = (w.num_blocks, 16, 2, oracle.prod_row_bytes(128, bits))
+    ref, near_i, near_s = oracle.write_prod(w.rows("k"), np.zeros(shape, np.uint8), w.slots, bits, signs, S)
+    pg = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+    api.write_kv_prod(ctx, torch.from_numpy(w.rows("k")).cuda(), pg, torch.from_numpy(w.slots).cuda(), bits,
+                      torch.from_numpy(S).cuda())
+    torch.cuda.synchronize()
+    got = pg.cpu().numpy()
+    keep = w.slots[w.slots >= 0]
+    _compare_rows(got[keep // 16, keep % 16], ref[keep // 16, keep % 16], near_i[keep // 16, keep % 16],
+                  near_s[keep // 16, keep % 16], bits, f"bits {bits}")
+    dropped_pages = np.ones(w.num_blocks * 16, bool)
+    dropped_pages[keep] = False
+    assert not got.reshape(w.num_blocks * 16, -1)[dropped_pages].any()  # skipped slots stay zero
+
+
+# lengths past 512 tokens span several 32-page chunks of the score kernel;
+# groups above 8 split a KV head's query heads over workgroups (12: a short tail)
+@pytest.mark.parametrize("bits,hkv,G,lens", [(4, 2, 8, [200, 17, 0, 64]), (3, 1, 4, [200, 17, 0, 64]),
+                                             (2, 4, 2, [200, 17, 0, 64]), (5, 2, 3, [200, 17, 0, 64]),
+                                             (4, 1, 12, [1100, 17, 0, 530]), (3, 2, 16, [600, 513, 1])])
+def test_scores_match_oracle(ctx, bits, hkv, G, lens):
+    w = workloads.make_workload(f"qjls{bits}", num_q_heads=hkv * G, num_kv_heads=hkv, seq_lens=lens,
+                                seed=120 + bits, outlier_frac=0.02)
+    print(f"[qjl] scores bits={bits} Hkv={hkv} G={G} lens={w.seq_lens.tolist()}", flush=True)
+    S = workloads.qjl_matrix(128, seed=20 + bits)
+    signs = oracle.rht_signs(42, 128)
+    shape = (w.num_blocks, 16, hkv, oracle.prod_row_bytes(128, bits))
+    pages, _, _ = oracle.write_prod(w.rows("k"), np.zeros(shape, np.uint8), w.slots, bits, signs, S)
+    q = w.queries()
+    ref = oracle.paged_prod_scores(q, pages, w.block_table, w.seq_lens, bits, signs, S)
+    got = api.prod_scores(ctx, torch.from_numpy(q).cuda(), torch.from_numpy(pages).cuda(),
+                          torch.from_numpy(w.block_table).cuda(), torch.from_numpy(w.seq_lens).cuda(), bits,
+                          torch.from_numpy(S).cuda())
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    norms = np.zeros(ref.shape)
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        assert not got[b, :, L:].any()
+        if L == 0:
+            continue
+        t = np.arange(L)
+        rows = pages[w.block_table[b, t // 16], t % 16]  # [L, Hkv, RB]
+        n = oracle.prod_bytes_to_rows(rows, bits, 128)[1].astype(np.float64)  # [L, Hkv]
+        norms[b, :, :L] = np.repeat(n.T, G, axis=0)
+    _check_scores(got, ref, q, norms, f"scores bits {bits}")
+
+
+def test_full_size_long_context(ctx):
+    # every K row of the long-context workload written as 4-bit prod rows on
+    # the GPU, then the scores of every head over all 131072 tokens of each
+    # sequence; sequence 0 checked row by row and score by score
+    w = workloads.preset("long_context")
+    bits = 4
+    print(f"[qjl] full size long_context: {w.num_tokens} tokens x {w.num_kv_heads} heads, prod {bits} bits",
+          flush=True)
+    S = workloads.qjl_matrix(128, seed=4)
+    signs = oracle.rht_signs(42, 128)
+    dev = torch.device("cuda")
+    pg = torch.zeros((w.num_blocks, 16, w.num_kv_heads, oracle.prod_row_bytes(128, bits)), dtype=torch.uint8,
+                     device=dev)
+    St = torch.from_numpy(S).to(dev)
+    api.write_kv_prod(ctx, torch.from_numpy(w.rows("k", threads=16)).to(dev), pg, torch.from_numpy(w.slots).to(dev),
+                      bits, St)
+    q = w.queries()
+    got = api.prod_scores(ctx, torch.from_numpy(q).to(dev), pg, torch.from_numpy(w.block_table).to(dev),
+                          torch.from_numpy(w.seq_lens).to(dev), bits, St, max_seq_len=w.max_seq_len)
+    torch.cuda.synchronize()
+    b = 0
+    L = int(w.seq_lens[b])
+    ref_pages, near_i, near_s, kept = sequence_prod_pages(w, b, bits, signs, S)
+    ids = torch.from_numpy(w.block_table[b, :L // 16].astype(np.int64)).to(dev)
+    gpu_pages = pg[ids].cpu().numpy()
+    _compare_rows(gpu_pages, ref_pages, near_i, near_s, bits, "long_context sequence 0")
+    bt = np.arange(ref_pages.shape[0], dtype=np.int32)[None]
+    ref = oracle.paged_prod_scores(q[b:b + 1], ref_pages, bt, np.array([L]), bits, signs, S)[0]
+    # rows whose indices or signs differ (the exemptions above) are excluded;
+    # gamma's last-place differences stay in (far inside the tolerance)
+    gi, _, gz, _ = oracle.prod_bytes_to_rows(gpu_pages.reshape(L, w.num_kv_heads, -1), bits, 128)
+    ri, _, rz, _ = oracle.prod_bytes_to_rows(ref_pages.reshape(L, w.num_kv_heads, -1), bits, 128)
+    same = np.all(gi == ri, axis=-1) & np.all(gz == rz, axis=-1)
+    G = w.num_q_heads // w.num_kv_heads
+    mask = np.repeat(same.T, G, axis=0)  # [Hq, L]
+    g = got[b].cpu().numpy()
+    n = oracle.prod_bytes_to_rows(ref_pages.reshape(L, w.num_kv_heads, -1), bits, 128)[1].astype(np.float64)
+    norms = np.repeat(n.T, G, axis=0)
+    print(f"  {int((~mask).sum())} of {mask.size} scores excluded (rows with exempt index mismatches)", flush=True)
+    _check_scores(np.where(mask, g, 0.0), np.where(mask, ref, 0.0), q[b], norms, "long_context sequence 0 scores")
