@@ -607,6 +607,7 @@ tq_status tq_prod_scores(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int
   if (!workspace || workspace_bytes < tq_prod_scores_workspace_bytes(batch, num_q_heads)) return TQ_ERR_WORKSPACE;
   const int row_bytes = (int)tq_prod_row_bytes(kHeadDim, bits);
   if ((long long)block_size * num_kv_heads * row_bytes > (1 << 30)) return TQ_ERR_UNSUPPORTED;
+  if ((long long)max_seq_len * 8 * sizeof(float) >= (1LL << 31)) return TQ_ERR_UNSUPPORTED;  // 8 score rows per buffer
   if (!device_is_gfx950()) return TQ_ERR_NO_DEVICE;
   tq::ProdScoreArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -629,7 +630,17 @@ tq_status tq_prod_scores(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int
   a.row_bytes = row_bytes;
   a.q_dtype = (int)q_dtype;
   std::memcpy(a.sign_bits, ctx->sign_bits, sizeof(a.sign_bits));
-  std::memcpy(a.cent, ctx->cent[bits - 1], sizeof(float) << (bits - 1));
+  for (int i = 0; i < (1 << (bits - 1)); ++i) a.cent[i] = 16.0f * ctx->cent[bits - 1][i];  // exact
+  // pages per workgroup: enough workgroups for the device (about 4 per CU),
+  // at most 128 pages each, a multiple of the 4 waves
+  const int npages = (max_seq_len + block_size - 1) / block_size;
+  const long long units = (long long)batch * num_kv_heads * ((num_q_heads / num_kv_heads + 7) / 8);
+  const long long per_seq = std::max(1LL, (4LL * device_cu_count() + units - 1) / units);
+  int cp = (int)std::min<long long>(128, (npages + per_seq - 1) / per_seq);
+  cp = std::max(4, (cp + 3) / 4 * 4);
+  a.chunk_pages = cp;
+  a.chunks = (npages + cp - 1) / cp;
+  a.vec_store = (max_seq_len % 4 == 0) && !(reinterpret_cast<uintptr_t>(scores) & 15);
   return hip_status(tq::launch_prod_scores(a, bits, (hipStream_t)stream));
 }
 

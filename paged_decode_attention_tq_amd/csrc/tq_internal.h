@@ -59,8 +59,11 @@ struct ProdScoreArgs {
   int32_t max_len;               // lengths are clamped to this (the block table's reach)
   int32_t row_bytes;
   int32_t q_dtype;
+  int32_t chunk_pages;           // pages per workgroup (a multiple of 4)
+  int32_t chunks;                // ceil(pages of max_seq_len / chunk_pages)
+  int32_t vec_store;             // scores rows 16-byte aligned (max_seq_len % 4 == 0, aligned base)
   uint32_t sign_bits[kHeadDim / 32];
-  float cent[16];                // the 2^(bits-1) centroids of the index codebook
+  float cent[16];                // the 2^(bits-1) centroids of the index codebook, times 16
 };
 
 // Arguments of the dense readback kernel (tq_decompress.hip).
