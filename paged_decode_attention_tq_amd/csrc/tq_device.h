@@ -74,6 +74,16 @@ __device__ __forceinline__ float cent_of_lane(const float* cent, int lane) {
   return v;
 }
 
+// 2^(13 - floor(log2 mx)): scales values of magnitude <= mx into [2^13, 2^14)
+// at most, where an fp16 hi + lo split keeps about 22 bits; 1 for mx = 0,
+// denormal, inf or nan.  Exact (a power of two).
+__device__ __forceinline__ float pow2_scale(float mx) {
+  const int e = (int)((__float_as_uint(mx) >> 23) & 0xFF);
+  if (e == 0 || e == 255) return 1.0f;
+  const int k = min(max(13 - (e - 127), -100), 100);
+  return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
 __device__ __forceinline__ uint32_t pack_half2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }

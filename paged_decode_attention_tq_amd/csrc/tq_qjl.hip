@@ -108,13 +108,6 @@ constexpr float kCentScale = 16.0f;  // the host passes centroids times 16 (exac
 constexpr int kNibBytes = 16 * 256;
 constexpr int kMaxChunkPages = 128;  // pages per workgroup at most (the host's choice)
 
-__device__ __forceinline__ float pow2_scale(float mx) {  // 2^(13 - floor(log2 mx)); 1 for 0, denormal, inf, nan
-  const int e = (int)((__float_as_uint(mx) >> 23) & 0xFF);
-  if (e == 0 || e == 255) return 1.0f;
-  const int k = min(max(13 - (e - 127), -100), 100);
-  return __uint_as_float((uint32_t)(k + 127) << 23);
-}
-
 // fp16 part (hi, or the rounding residual lo) of the 32 scaled values of v
 // as 16 pairs
 __device__ __forceinline__ void split_pairs(const float (&v)[32], float s, bool lo, uint32_t (&out)[16]) {

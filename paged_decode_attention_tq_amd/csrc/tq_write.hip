@@ -57,6 +57,39 @@ __device__ __forceinline__ void load_row32(const void* raw, int64_t elem_off, fl
   }
 }
 
+// The same row slice as raw words: loads issued now, widened later.
+template <int DT>
+struct RawSlice {
+  u32x4 v[DT == 0 ? 8 : 4];
+};
+
+template <int DT>
+__device__ __forceinline__ void fetch_raw(const void* raw, int64_t elem_off, RawSlice<DT>& r) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(raw) + elem_off * (DT == 0 ? 4 : 2));
+#pragma unroll
+  for (int i = 0; i < (DT == 0 ? 8 : 4); ++i) r.v[i] = p[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void widen_raw(const RawSlice<DT>& r, float (&x)[32]) {
+#pragma unroll
+  for (int i = 0; i < (DT == 0 ? 8 : 4); ++i) {
+    const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (DT == 0) {
+        x[4 * i + k] = __uint_as_float(w[k]);
+      } else if constexpr (DT == 1) {
+        x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] & 0xFFFF));
+        x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[k] >> 16));
+      } else {
+        x[8 * i + 2 * k] = bf16_to_f32((uint16_t)(w[k] & 0xFFFF));
+        x[8 * i + 2 * k + 1] = bf16_to_f32((uint16_t)(w[k] >> 16));
+      }
+    }
+  }
+}
+
 // n = fp32(sqrt(sum x^2)) of the quad's row, the sum exact-rounded in
 // float64: the fast sum has relative error below 40 * 2^-53 (the sqrt halves
 // it); when that bound does not decide the fp32 rounding, the row is re-summed
@@ -199,86 +232,113 @@ __global__ __launch_bounds__(256) void write_pair_kernel(WriteArgs k, WriteArgs 
 // the d x d matrix S (sign of (S e)_i), and gamma = ||e||.  Row: index words,
 // norm, 4 sign words (bit i of word q = sign of output 32 q + i), gamma.
 //
-// Quad per row as above.  Lane q forms outputs 32 q .. 32 q + 31 of S e: it
-// takes the 32 residuals of each quad lane in turn (DPP broadcasts) and
-// multiplies by its 32 x 32 block of S from LDS (kSkGroup below: the four
-// quad lanes' reads fall on different banks).  Persistent grid: S is loaded
-// once per workgroup.
+// A workgroup takes 64 rows at a time.  The front end is the MSE writer's,
+// a quad per row (load, norm, rotation, boundary count), and leaves the
+// residual in the quad's registers; they go to LDS as fp16 hi + lo after a
+// power-of-two scaling per row.  The sketch P = E S^T of the 64 rows is a
+// dense product on MFMA (v_mfma_f32_16x16x32_f16): wave w forms outputs
+// 32 w .. 32 w + 31 of every row, with its 32 rows of S (fp16 hi + lo, a
+// power-of-two scale per row) held in registers for the whole launch, as
+// e_hi s_hi + e_lo s_hi + e_hi s_lo (the dropped lo lo term is below 2^-22
+// of sum_j |S_ij e_j|).  Positive scales leave every sign as it is.  The
+// signs are OR-ed across lanes into word w of each row, and the front
+// end's quads store whole rows.  Persistent grid; a quad's next raw row is
+// loaded while the current block's sketch runs.
 // ==========================================================================
-// S in LDS: rows 32 g .. 32 g + 31 at g * kSkGroup floats, row-major inside;
-// the 4-float gap between groups puts the four quad lanes' reads on
-// different banks
-constexpr int kSkGroup = 32 * kHeadDim + 4;
-
-template <int K>
-__device__ __forceinline__ float quad_bcast(float v) {
-  constexpr int ctrl = K | (K << 2) | (K << 4) | (K << 6);
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
-}
-
-// p[i] += sum_j S[32 q + i][32 K + j] e_K[j], e_K the residuals of quad lane K
-template <int K>
-__device__ __forceinline__ void sketch_part(const float* sk, int q, const float (&x)[32], float (&p)[32]) {
-  float ek[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) ek[j] = quad_bcast<K>(x[j]);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float* srow = sk + q * kSkGroup + i * kHeadDim + 32 * K;  // constant offsets from one base
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const floatx4 s4 = *reinterpret_cast<const floatx4*>(srow + 4 * m);
-      p[i] = fmaf(s4[0], ek[4 * m], p[i]);
-      p[i] = fmaf(s4[1], ek[4 * m + 1], p[i]);
-      p[i] = fmaf(s4[2], ek[4 * m + 2], p[i]);
-      p[i] = fmaf(s4[3], ek[4 * m + 3], p[i]);
-    }
-    // one output row at a time: p[i] is complete before the next row's reads
-    // are issued (the compiler would otherwise gather all 256 reads of the
-    // block first, more values than the register file holds)
-    asm volatile("" : "+v"(p[i]) :: "memory");
-  }
-}
+// E stage row stride in halves: 16 bytes of padding put the 16 rows that a
+// quarter-wave of ds_read_b128 reads on distinct banks
+constexpr int kEStride = 136;
 
 template <int BITS, int DT>
-__global__ __launch_bounds__(256) void write_prod_kernel(ProdWriteArgs pa) {
+__global__ __launch_bounds__(256, 2) void write_prod_kernel(ProdWriteArgs pa) {  // two workgroups per CU
   constexpr int MB = BITS - 1, N = 1 << MB, HALF = N / 2;
-  __shared__ float sk[4 * kSkGroup];
+  __shared__ __align__(16) _Float16 ehi[64 * kEStride];
+  __shared__ __align__(16) _Float16 elo[64 * kEStride];
+  __shared__ uint32_t sgn[64 * 5];
   const WriteArgs& a = pa.w;
-  for (int e = threadIdx.x; e < kHeadDim * kHeadDim / 4; e += 256) {
-    const int i = (4 * e) >> 7, j = (4 * e) & 127;
-    *reinterpret_cast<floatx4*>(sk + (i >> 5) * kSkGroup + (i & 31) * kHeadDim + j) =
-        *reinterpret_cast<const floatx4*>(pa.sketch + 4 * e);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = tid & 3, rl = tid >> 2;     // front end: quad lane, row of the 64
+  const int n = lane & 15, c = lane >> 4;   // MFMA: row / column n, k-slots 8 c .. 8 c + 7
+  const uint32_t bit_lo = 1u << n, bit_hi = 1u << (n + 16);
+
+  // B operand: S rows 32 wave + 16 t + n, coordinates 32 ks + 8 c .. + 7
+  half8 sh[2][4], sl[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float* srow = pa.sketch + (int64_t)(32 * wave + 16 * t + n) * kHeadDim + 8 * c;
+    float v[4][8];
+    float mx = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const floatx4 v0 = *reinterpret_cast<const floatx4*>(srow + 32 * ks);
+      const floatx4 v1 = *reinterpret_cast<const floatx4*>(srow + 32 * ks + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[ks][j] = v0[j], v[ks][4 + j] = v1[j];
+        mx = fmaxf(mx, fmaxf(__builtin_fabsf(v0[j]), __builtin_fabsf(v1[j])));
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float sc = pow2_scale(mx);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float y = v[ks][j] * sc;
+        const _Float16 h = (_Float16)y;
+        sh[t][ks][j] = h;
+        sl[t][ks][j] = (_Float16)(y - (float)h);
+      }
+    }
   }
-  __syncthreads();
-  const int q = threadIdx.x & 3;
+
   const int64_t nblk = (a.num_rows + 63) / 64;
+  // the raw slice and slot of this quad's row of block b, requested one
+  // block ahead (in flight during the previous block's sketch and stores)
+  RawSlice<DT> pre;
+  int64_t pre_slot = -1;
+  auto issue = [&](int64_t b) {
+    const int64_t row = b * 64 + rl;
+    if (b < nblk && row < a.num_rows) {  // uniform per quad
+      pre_slot = a.slots[row / a.num_kv_heads];
+      fetch_raw<DT>(a.raw, row * kHeadDim + 32 * q, pre);
+    }
+  };
+  issue(blockIdx.x);
   for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    const int64_t row = blk * 64 + (threadIdx.x >> 2);
-    if (row >= a.num_rows) continue;  // uniform per quad
-    const int64_t tok = row / a.num_kv_heads;
-    const int head = (int)(row - tok * a.num_kv_heads);
-    const int64_t slot = a.slots[tok];
+    // ---- front end: row blk * 64 + rl on quad rl ---------------------------
+    const int64_t row = blk * 64 + rl;
+    int64_t slot = -1;
+    int head = 0;
     float x[32];
-    load_row32<DT>(a.raw, row * kHeadDim + 32 * q, x);
-    if (slot < 0) continue;
-    if (slot >= a.num_slots) {
-      if (q == 0 && head == 0 && a.err_count) atomicAdd(a.err_count, 1);
-      continue;
+    if (row < a.num_rows) {  // uniform per quad
+      head = (int)(row % a.num_kv_heads);
+      slot = pre_slot;
+      widen_raw<DT>(pre, x);
+      if (slot >= a.num_slots) {
+        if (q == 0 && head == 0 && a.err_count) atomicAdd(a.err_count, 1);
+        slot = -1;
+      }
+    }
+    if (slot < 0) {  // nothing to store: the row's work runs on zeros
+#pragma unroll
+      for (int j = 0; j < 32; ++j) x[j] = 0.0f;
     }
     const double n64 = row_norm(x);
     const float n32 = (float)n64;
-    const float c = n64 > 0.0 ? (float)(1.0 / (n64 * 11.313708498984761)) : 0.0f;  // 1/(n sqrt(128))
+    const float cn = n64 > 0.0 ? (float)(1.0 / (n64 * 11.313708498984761)) : 0.0f;  // 1/(n sqrt(128))
     rotate_row(a.sign_bits, q, x);
 
     // indices at MB bits and the residual (kept in x), its squared norm
     uint32_t w[MB];
 #pragma unroll
     for (int k = 0; k < MB; ++k) w[k] = 0;
-    float ss = 0.0f;
+    float ss = 0.0f, mx = 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      const float r = x[j] * c;
+      const float r = x[j] * cn;
       const float ar = __builtin_fabsf(r);
       int cnt = 0;
 #pragma unroll
@@ -292,32 +352,79 @@ __global__ __launch_bounds__(256) void write_prod_kernel(ProdWriteArgs pa) {
       for (int k = 1; k < HALF; ++k) cp = cnt == k ? pa.cpos[k] : cp;
       x[j] = r - (r > 0.0f ? cp : -cp);
       ss = fmaf(x[j], x[j], ss);
+      mx = fmaxf(mx, __builtin_fabsf(x[j]));
     }
     ss += quad_xor<1>(ss);
     ss += quad_xor<2>(ss);
     const float gamma = __builtin_sqrtf(ss);
+    mx = fmaxf(mx, quad_xor<1>(mx));
+    mx = fmaxf(mx, quad_xor<2>(mx));
+    {
+      // the residual, scaled by a power of two, as fp16 hi and lo
+      const float sc = pow2_scale(mx);
+      uint32_t hw[16], lw[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float y0 = x[2 * j] * sc, y1 = x[2 * j + 1] * sc;
+        const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+        hw[j] = pack_half2(h0, h1);
+        lw[j] = pack_half2((_Float16)(y0 - (float)h0), (_Float16)(y1 - (float)h1));
+      }
+      u32x4* dh = reinterpret_cast<u32x4*>(ehi + rl * kEStride + 32 * q);
+      u32x4* dl = reinterpret_cast<u32x4*>(elo + rl * kEStride + 32 * q);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        dh[k] = u32x4{hw[4 * k], hw[4 * k + 1], hw[4 * k + 2], hw[4 * k + 3]};
+        dl[k] = u32x4{lw[4 * k], lw[4 * k + 1], lw[4 * k + 2], lw[4 * k + 3]};
+      }
+    }
+    __syncthreads();
+    issue(blk + gridDim.x);
 
-    // outputs 32 q + i of S e
-    float p[32];
+    // ---- sketch: outputs 32 wave .. 32 wave + 31 of the 64 rows ------------
 #pragma unroll
-    for (int i = 0; i < 32; ++i) p[i] = 0.0f;
-    sketch_part<0>(sk, q, x, p);
-    sketch_part<1>(sk, q, x, p);
-    sketch_part<2>(sk, q, x, p);
-    sketch_part<3>(sk, q, x, p);
-    uint32_t zw = 0;
+    for (int rt = 0; rt < 4; ++rt) {
+      floatx4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) zw |= (p[i] >= 0.0f ? 1u : 0u) << i;
+      for (int ks = 0; ks < 4; ++ks) {
+        const int at = (16 * rt + n) * kEStride + 32 * ks + 8 * c;
+        const half8 ah = *reinterpret_cast<const half8*>(ehi + at);
+        const half8 al = *reinterpret_cast<const half8*>(elo + at);
+        p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, sh[0][ks], p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, sh[1][ks], p1, 0, 0, 0);
+        p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, sh[0][ks], p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, sh[1][ks], p1, 0, 0, 0);
+        p0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, sl[0][ks], p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, sl[1][ks], p1, 0, 0, 0);
+      }
+      // lane (n, c) holds rows 16 rt + 4 c + r of outputs 32 wave + n (p0)
+      // and 32 wave + 16 + n (p1): bits n and n + 16 of the row's word
+      // `wave`, OR-ed across the 16 lanes of the row group
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t v = (p0[r] >= 0.0f ? bit_lo : 0u) | (p1[r] >= 0.0f ? bit_hi : 0u);
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
+        v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+        if (n == 0) sgn[(16 * rt + 4 * c + r) * 5 + wave] = v;
+      }
+    }
+    __syncthreads();
 
-    uint8_t* dst = a.pages + (slot / a.block_size) * a.page_bytes +
-                   ((slot % a.block_size) * a.num_kv_heads + head) * (int64_t)a.row_bytes;
-    uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+    // ---- the whole row -------------------------------------------------------
+    if (slot >= 0) {
+      const uint32_t zw = sgn[rl * 5 + q];
+      uint8_t* dst = a.pages + (slot / a.block_size) * a.page_bytes +
+                     ((slot % a.block_size) * a.num_kv_heads + head) * (int64_t)a.row_bytes;
+      uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
 #pragma unroll
-    for (int k = 0; k < MB; ++k) d32[MB * q + k] = w[k];
-    d32[4 * MB + 1 + q] = zw;
-    if (q == 3) {
-      d32[4 * MB] = __float_as_uint(n32);
-      d32[4 * MB + 5] = __float_as_uint(gamma);
+      for (int k = 0; k < MB; ++k) d32[MB * q + k] = w[k];
+      d32[4 * MB + 1 + q] = zw;
+      if (q == 3) {
+        d32[4 * MB] = __float_as_uint(n32);
+        d32[4 * MB + 5] = __float_as_uint(gamma);
+      }
     }
   }
 }
@@ -325,7 +432,7 @@ __global__ __launch_bounds__(256) void write_prod_kernel(ProdWriteArgs pa) {
 template <int BITS>
 static hipError_t launch_prod_bits(const ProdWriteArgs& a, int dt, int num_cus, hipStream_t st) {
   const int64_t nblk = (a.w.num_rows + 63) / 64;
-  const dim3 grid((unsigned)std::min<int64_t>(nblk, 2LL * num_cus)), block(256);  // 64 KB of LDS: two per CU
+  const dim3 grid((unsigned)std::min<int64_t>(nblk, 2LL * num_cus)), block(256);  // two per CU (registers)
   if (dt == 0)
     hipLaunchKernelGGL((write_prod_kernel<BITS, 0>), grid, block, 0, st, a);
   else if (dt == 1)
