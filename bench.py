@@ -147,6 +147,22 @@ def traffic_bytes(config):
     return prof.get("configs", {}).get(config, {}).get("bytes_per_call")
 
 
+def prod_traffic_bytes(config):
+    """HBM bytes per tq_prod_scores call of this config from the committed
+    counter profile, if it was taken on the current prod sources (else None)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "prod_traffic.json")
+    try:
+        prof = json.load(open(path))
+        digest = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in prof["sources"])).hexdigest()
+    except (OSError, ValueError, KeyError, TypeError):
+        return None
+    if prof.get("prod_sources_sha256") != digest:
+        return None
+    return prof.get("configs", {}).get(config, {}).get("scores_bytes_per_call")
+
+
 def cpu_decompress_baseline(w, kp_host, seconds=15.0):
     """Time the oracle's readback (``oracle.decompress_kv``) on a bounded
     sample: blocks of 2048 tokens (all KV heads) of the workload's slots,
@@ -237,6 +253,32 @@ def bench_decompress(args, torch, api, w, ctx, kp, slots):
     return result
 
 
+def cpu_prod_baseline(w, q, S, bits, seconds=15.0):
+    """Time the oracle's estimator (``oracle.prod_scores``) on a bounded
+    sample: the first 2048 tokens of sequence 0, written as prod rows by the
+    oracle (untimed), scored against each KV head's query group in turn until
+    about ``seconds`` have been spent; scores/s."""
+    import oracle
+
+    signs = oracle.rht_signs(w.rht_seed, w.head_dim)
+    raw = w.seq_rows("k", 0)[:2048]
+    T, Hkv = raw.shape[0], w.num_kv_heads
+    RB = oracle.prod_row_bytes(w.head_dim, bits)
+    pages = np.zeros(((T + 15) // 16, 16, Hkv, RB), dtype=np.uint8)
+    pages, _, _ = oracle.write_prod(raw, pages, np.arange(T, dtype=np.int64), bits, signs, S)
+    rows = pages.reshape(-1, Hkv, RB)[:T]
+    G = w.num_q_heads // Hkv
+    n, i, t0 = 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        g = i % Hkv
+        oracle.prod_scores(q[0, g * G:(g + 1) * G], rows[:, g], bits, signs, S)
+        n += G * T
+        i += 1
+    el = time.perf_counter() - t0
+    return {"value": n / el, "unit": "scores/s", "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{i} calls of {T} tokens x {G} query heads (sequence 0, one KV head each), {el:.1f} s"}
+
+
 def bench_prod(args, torch, api, w, ctx, kraw_d, slots, q):
     """The prod key codec on the workload's K rows: the writer over every row,
     then the inner-product scores of every query head over every key, timed
@@ -293,7 +335,7 @@ def bench_prod(args, torch, api, w, ctx, kraw_d, slots, q):
         "unit": "scores/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": float(sms.mean()),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": f"u8 prod rows ({bits - 1}-bit indices + 1-bit sketch), fp32 arithmetic",
+        "dtype": f"u8 prod rows ({bits - 1}-bit indices + 1-bit sketch); fp16 hi+lo MFMA operands, fp32 accumulation",
         "data": "synthetic (the workload's K rows; a seeded Gaussian sketch matrix)",
         "config": {"workload": f"{w.name} K rows as {bits}-bit prod rows: {w.num_tokens} tokens x Hkv {Hkv}, "
                                f"Hq {Hq}, head_dim {d}, block 16"},
@@ -302,8 +344,10 @@ def bench_prod(args, torch, api, w, ctx, kraw_d, slots, q):
         "writer_gbps": wbytes / (float(wms.mean()) / 1e3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": "tq_prod_scores (prod_query_kernel + prod_scores_kernel)",
                      "achieved": sbytes / ssec / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": sbytes / ssec / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": sbytes, "traffic": None},
-        "cpu_baseline": None,
+                     "frac": sbytes / ssec / 1e9 / HBM_PEAK_GBPS, "algorithmic_bytes": sbytes,
+                     "traffic": prod_traffic_bytes(w.name)},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_prod_baseline(
+            w, q, workloads.qjl_matrix(d, seed=0), bits, min(args.cpu_seconds, 15.0)),
     }
 
 
