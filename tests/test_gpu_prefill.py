@@ -32,14 +32,18 @@ def _queries(w, Lq, dt, seed):
 
 
 # (KV heads, group, lengths, query lengths, Lq): the decode of the prefix runs
-# on the wave kernel (group x Lq <= 8), as one workgroup, or staged; mixed
-# batches with one-token and empty chunks; a chunk of one page and more
+# on the wave kernel (group x Lq <= 8), as one workgroup, or staged (64 query
+# rows per KV head; 12 with a half-filled second query group; 32 with
+# prefixes of a few tokens); mixed batches with one-token and empty chunks; a
+# chunk of one page and more
 CASES = [
     (2, 2, [300, 45, 129, 9], [4, 1, 3, 0], 4),
     (1, 2, [40, 7, 3], [3, 2, 3], 3),
     (2, 8, [700, 33, 1500], [8, 5, 1], 8),
     (4, 4, [64, 200], [16, 1], 16),
     (2, 8, [90, 16, 17], [1, 1, 1], 1),
+    (3, 3, [1000, 17, 33], [4, 4, 2], 4),
+    (1, 16, [520, 2, 3], [1, 2, 2], 2),
 ]
 
 
@@ -68,6 +72,30 @@ def test_prefill_matches_oracle(ctx, case, dt):
         assert not got[b, n:].any(), f"rows past q_lens[{b}] = {n} are not zero"
     res = compare_decode(got.reshape(-1, w.num_q_heads, 128), ref.reshape(-1, w.num_q_heads, 128),
                          f"prefill case {case} {dt}")
+    print(f"  max|d| relL2 {res}", flush=True)
+
+
+@pytest.mark.parametrize("kb,vb", [(3, 5), (2, 3), (5, 2)])
+def test_prefill_multi_query_bit_widths(ctx, kb, vb):
+    # 16 query rows per KV head (two query groups) with other K / V index
+    # widths: 3- and 5-bit fields straddle bytes and words
+    lens, ql, Lq = [300, 90, 47], [4, 3, 1], 4
+    w = workloads.make_workload(f"prebits{kb}{vb}", num_q_heads=8, num_kv_heads=2, seq_lens=lens, seed=70 + kb + vb,
+                                outlier_frac=0.02)
+    print(f"[prefill] multi-query K{kb}/V{vb} lens={lens} q_lens={ql}", flush=True)
+    codec = oracle.OracleCodec(128, 42)
+    kp, _ = codec.write_kv(w.rows("k"), w.zero_pages(kb), w.slots, kb)
+    vp, _ = codec.write_kv(w.rows("v"), w.zero_pages(vb), w.slots, vb)
+    tq, q = _queries(w, Lq, "fp16", kb * 10 + vb)
+    ref = oracle.paged_prefill(q, np.array(ql), kp, vp, w.block_table, w.seq_lens, kb, vb, codec.signs,
+                               codec.centroids32(kb), codec.centroids32(vb))
+    out = api.paged_prefill(ctx, tq.cuda(), torch.tensor(ql, dtype=torch.int32).cuda(), torch.from_numpy(kp).cuda(),
+                            torch.from_numpy(vp).cuda(), torch.from_numpy(w.block_table).cuda(),
+                            torch.from_numpy(w.seq_lens).cuda(), kb, vb)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    res = compare_decode(got.reshape(-1, w.num_q_heads, 128), ref.reshape(-1, w.num_q_heads, 128),
+                         f"prefill multi-query K{kb}/V{vb}")
     print(f"  max|d| relL2 {res}", flush=True)
 
 
