@@ -24,6 +24,7 @@ __all__ = [
     "write_kv_pair",
     "prod_row_bytes",
     "write_kv_prod",
+    "prod_scores_workspace_bytes",
     "prod_scores",
     "decompress_kv",
     "decode_workspace_bytes",
@@ -192,6 +193,11 @@ def write_kv_prod(ctx: Context, raw: torch.Tensor, pages: torch.Tensor, slots: t
     return 0
 
 
+def prod_scores_workspace_bytes(batch: int, num_q_heads: int) -> int:
+    """Bytes of device workspace ``prod_scores`` needs (rotated queries and their sketches)."""
+    return int(_lib.lib().tq_prod_scores_workspace_bytes(batch, num_q_heads))
+
+
 def prod_scores(ctx: Context, q: torch.Tensor, pages: torch.Tensor, block_table: torch.Tensor,
                 seq_lens: torch.Tensor, bits: int, sketch: torch.Tensor, max_seq_len: int | None = None,
                 out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -213,7 +219,7 @@ def prod_scores(ctx: Context, q: torch.Tensor, pages: torch.Tensor, block_table:
         out = torch.empty((B, Hq, max_seq_len), dtype=torch.float32, device=q.device)
     _need(out.dtype == torch.float32 and out.shape == (B, Hq, max_seq_len) and out.is_contiguous(),
           "out must be fp32 [B, Hq, max_seq_len]")
-    need = int(_lib.lib().tq_prod_scores_workspace_bytes(B, Hq))
+    need = prod_scores_workspace_bytes(B, Hq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     st = _lib.lib().tq_prod_scores(

@@ -1,4 +1,4 @@
-"""The write and decode calls inside a captured HIP graph.
+"""The library's calls inside a captured HIP graph.
 
 The library never allocates and never synchronises inside tq_write_kv_pair
 and tq_paged_decode (the caller owns out, the workspace and err_count), so a
@@ -138,6 +138,55 @@ def test_graph_readback_hybrid_and_multi_query(ctx):
         g.replay()
         torch.cuda.synchronize()
         for got, want in zip((dense, hout, pout), eager):
+            assert torch.equal(got, want), f"replay {r} differs from the eager call"
+        del junk
+    assert int(err.item()) == 0
+
+
+def test_graph_prod_codec(ctx):
+    # the prod key codec's writer and scores captured together: every replay
+    # (pages cleared and scores overwritten in between) equal to the eager
+    # calls bit for bit
+    w = workloads.make_workload("graphp", num_q_heads=16, num_kv_heads=2, seq_lens=[700, 33, 150], seed=45)
+    print(f"[graph] prod writer + scores lens={w.seq_lens.tolist()}", flush=True)
+    dev = torch.device("cuda")
+    bits = 4
+    pages = torch.zeros((w.num_blocks, 16, 2, api.prod_row_bytes(128, bits)), dtype=torch.uint8, device=dev)
+    slots = torch.from_numpy(w.slots).to(dev)
+    raw = torch.from_numpy(w.rows("k")).to(dev)
+    S = torch.from_numpy(workloads.qjl_matrix(128, seed=5)).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    q = torch.from_numpy(w.queries()).to(dev)
+    scores = torch.empty((w.batch, w.num_q_heads, w.max_seq_len), dtype=torch.float32, device=dev)
+    ws = torch.empty(api.prod_scores_workspace_bytes(w.batch, w.num_q_heads), dtype=torch.uint8, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        api.write_kv_prod(ctx, raw, pages, slots, bits, S, err_count=err, check_slots=False)
+        api.prod_scores(ctx, q, pages, bt, lens, bits, S, max_seq_len=w.max_seq_len, out=scores, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [pages.clone(), scores.clone()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        pages.zero_()
+        scores.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((pages, scores), eager):
             assert torch.equal(got, want), f"replay {r} differs from the eager call"
         del junk
     assert int(err.item()) == 0
