@@ -181,8 +181,10 @@ size_t tq_prod_row_bytes(int head_dim, int bits);
  * tq_prod_row_bytes rows, errors and err_count).  sketch: device fp32
  * [head_dim, head_dim] row-major, 16-byte aligned: the matrix S, an input
  * (the method's random draw).  gamma is computed in fp32 from the fp32
- * residual; the sign of a projection within fp32 rounding of zero may differ
- * from an exact computation.  bits 2..5.  Asynchronous, allocates nothing. */
+ * residual; the projection S e is formed from fp16 hi + lo parts of e and S
+ * with fp32 accumulation (error about 2^-22 of sum_j |S_ij e_j|), so the sign
+ * of a projection that close to zero may differ from an exact computation.
+ * bits 2..5.  Asynchronous, allocates nothing. */
 tq_status tq_write_kv_prod(const tq_ctx* ctx, const void* raw, tq_dtype raw_dtype,
                            int64_t num_tokens, int num_kv_heads, uint8_t* pages,
                            int64_t num_blocks, int block_size, const int64_t* slots,
@@ -205,6 +207,8 @@ size_t tq_prod_scores_workspace_bytes(int batch, int num_q_heads);
  *   scores      device, fp32 [batch, num_q_heads, max_seq_len]; entries past a
  *               sequence's length are written as 0.
  *   workspace   device, >= tq_prod_scores_workspace_bytes(...), 16-byte aligned.
+ * Products of fp16 hi + lo parts with fp32 accumulation (about fp32
+ * accuracy).  max_seq_len must stay below 2^26 (TQ_ERR_UNSUPPORTED).
  * Asynchronous, allocates nothing; errors as tq_paged_decode. */
 tq_status tq_prod_scores(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
                          int num_q_heads, int num_kv_heads, const uint8_t* pages, int bits,

@@ -106,6 +106,8 @@ def test_status_strings_and_argument_errors():
     assert ps(h, a64, 1, 2, 8, 2, a64, 7, 8, 16, a64, 4, a64, 64, a64, a64, a64, wsb, None) == 2  # bits 7
     assert ps(h, a64, 1, 2, 8, 2, a64, 4, 8, 16, a64, 4, a64, 64, None, a64, a64, wsb, None) == 1  # no sketch
     assert ps(h, a64, 1, 2, 8, 3, a64, 4, 8, 16, a64, 4, a64, 64, a64, a64, a64, wsb, None) == 1  # 8 % 3
+    assert ps(h, a64, 1, 2, 8, 2, a64, 4, 8, 16, a64, 1 << 22, a64, 1 << 26, a64, a64, a64, wsb,
+              None) == 2  # 2^26 score columns
     # multi-query attention
     pf = lib.tq_paged_prefill
     a256 = ctypes.c_void_p(256)
