@@ -95,6 +95,66 @@ def cpu_baseline(w, kraw, vraw, q, seconds=15.0):
     }
 
 
+def _oracle_sample(w, kraw, vraw, Ls):
+    """The oracle writer's pages of the first ``Ls`` tokens of sequence 0 (all
+    KV heads, identity block table) and the time the write took."""
+    import oracle
+
+    codec = oracle.OracleCodec(w.head_dim, w.rht_seed)
+    lo = int(w.cu_seqlens[0])
+    npg = (Ls + w.block_size - 1) // w.block_size
+    slots = np.arange(Ls, dtype=np.int64)
+    kp = np.zeros((npg, w.block_size, w.num_kv_heads, w.row_bytes(w.k_bits)), dtype=np.uint8)
+    vp = np.zeros((npg, w.block_size, w.num_kv_heads, w.row_bytes(w.v_bits)), dtype=np.uint8)
+    t0 = time.perf_counter()
+    kp, _ = codec.write_kv(kraw[lo:lo + Ls], kp, slots, w.k_bits)
+    vp, _ = codec.write_kv(vraw[lo:lo + Ls], vp, slots, w.v_bits)
+    return codec, kp, vp, np.arange(npg, dtype=np.int32)[None], time.perf_counter() - t0
+
+
+def cpu_path_baseline(w, kraw, vraw, seconds, call, per_step, unit, what):
+    """Time an oracle attention function on the first ``Ls`` tokens of
+    sequence 0, one KV head (its pages' head slice and its query heads) per
+    call, until about ``seconds`` have been spent; the time of one KV head is
+    scaled to a full step (every KV head of every sequence, the full
+    context).  ``call(codec, kp, vp, bt, Ls, g)`` runs the oracle for KV head
+    g; ``per_step`` is the step's count in ``unit``."""
+    L = int(w.seq_lens[0])
+    Ls = min(L, 32768)
+    codec, kp, vp, bt, t_write = _oracle_sample(w, kraw, vraw, Ls)
+    t_run, heads = 0.0, 0
+    for g in range(w.num_kv_heads):
+        kg = np.ascontiguousarray(kp[:, :, g:g + 1])
+        vg = np.ascontiguousarray(vp[:, :, g:g + 1])
+        ts = time.perf_counter()
+        call(codec, kg, vg, bt, Ls, g)
+        t_run += time.perf_counter() - ts
+        heads += 1
+        if t_run > seconds:
+            break
+    t_step = t_run / heads * w.num_kv_heads * w.batch * (L / Ls)
+    return {"value": per_step / t_step, "unit": unit, "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"sequence 0, first {Ls} of {L} tokens, {heads} of {w.num_kv_heads} KV heads by {what} "
+                      f"(float64) in {t_run:.1f} s, scaled to {w.batch} sequences x {L} tokens x "
+                      f"{w.num_kv_heads} KV heads; oracle write of the sample took {t_write:.1f} s"}
+
+
+def op_traffic_bytes(op, key):
+    """HBM bytes per call of an op on a workload from the committed counter
+    profiles, if they were taken on the op's current sources (else None)."""
+    import hashlib
+
+    try:
+        prof = json.load(open(os.path.join(ROOT, "profiles", "op_traffic.json")))
+        rec = prof["ops"][op]
+        digest = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])).hexdigest()
+    except (OSError, ValueError, KeyError, TypeError):
+        return None
+    if rec.get("sources_sha256") != digest:
+        return None
+    return rec.get("bytes_per_call", {}).get(key)
+
+
 def stream_read_ceiling(torch, dev, gib=2, reps=10):
     """Practical HBM read ceiling on this device: the streaming-read probe
     (csrc/probe/tq_stream_probe.hip, 16-byte non-temporal loads, 1 KB per wave
@@ -243,7 +303,7 @@ def bench_decompress(args, torch, api, w, ctx, kp, slots):
             "unit": "GB/s",
             "frac": nbytes / sec / 1e9 / HBM_PEAK_GBPS,
             "algorithmic_bytes": nbytes,
-            "traffic": None,
+            "traffic": op_traffic_bytes("decompress", f"{w.name}/{args.out_dtype}"),
         },
         "cpu_baseline": None,
     }
@@ -561,7 +621,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None if (hybrid or prefill) else traffic_bytes(w.name),
+            "traffic": (op_traffic_bytes("hybrid", f"{w.name}/window{args.window}") if hybrid else
+                        op_traffic_bytes("prefill", f"{w.name}/q{args.q_len}") if prefill else traffic_bytes(w.name)),
         },
         "prefill_write": write,
         "stream_read_ceiling": None,
@@ -573,9 +634,36 @@ def main():
             f"{result['stream_read_ceiling']['mean_gbps']:.0f} GB/s mean")
     if hybrid:
         result["window_bytes"] = window_bytes
-    if not args.no_cpu_baseline and not hybrid and not prefill:
+    if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(w, kraw, vraw, q, args.cpu_seconds)
+        if hybrid:
+            import oracle
+
+            rkh, rvh, rlh = rk[:1], rv[:1], rl[:1]
+            G = Hq // Hkv
+
+            def hyb(codec, kg, vg, bt, Ls, g):
+                oracle.paged_decode_hybrid(q[:1, g * G:(g + 1) * G], kg, vg, bt, np.array([Ls]),
+                                           rkh[:, :, g:g + 1], rvh[:, :, g:g + 1], rlh, w.k_bits, w.v_bits,
+                                           codec.signs, codec.centroids32(w.k_bits), codec.centroids32(w.v_bits))
+
+            result["cpu_baseline"] = cpu_path_baseline(w, kraw, vraw, args.cpu_seconds, hyb, B, "decode tokens/s",
+                                                       "oracle.paged_decode_hybrid with the sequence's window")
+        elif prefill:
+            import oracle
+
+            pqh = pq[:1].float().cpu().numpy()
+            G = Hq // Hkv
+
+            def pre(codec, kg, vg, bt, Ls, g):
+                oracle.paged_prefill(pqh[:, :, g * G:(g + 1) * G], np.array([Lq]), kg, vg, bt, np.array([Ls]),
+                                     w.k_bits, w.v_bits, codec.signs, codec.centroids32(w.k_bits),
+                                     codec.centroids32(w.v_bits))
+
+            result["cpu_baseline"] = cpu_path_baseline(w, kraw, vraw, args.cpu_seconds, pre, B * Lq,
+                                                       "query tokens/s", f"oracle.paged_prefill ({Lq} queries)")
+        else:
+            result["cpu_baseline"] = cpu_baseline(w, kraw, vraw, q, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
