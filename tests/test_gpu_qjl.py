@@ -153,3 +153,53 @@ def test_full_size_long_context(ctx):
     norms = np.repeat(n.T, G, axis=0)
     print(f"  {int((~mask).sum())} of {mask.size} scores excluded (rows with exempt index mismatches)", flush=True)
     _check_scores(np.where(mask, g, 0.0), np.where(mask, ref, 0.0), q[b], norms, "long_context sequence 0 scores")
+
+
+def test_scores_bad_block_ids_read_zero_rows(ctx):
+    # block ids outside [0, num_blocks) in the table read as zero rows: those
+    # tokens score 0, every other token keeps the oracle's estimate
+    bits = 4
+    w = workloads.make_workload("qjlbad", num_q_heads=8, num_kv_heads=2, seq_lens=[300, 90], seed=131)
+    S = workloads.qjl_matrix(128, seed=9)
+    signs = oracle.rht_signs(42, 128)
+    shape = (w.num_blocks, 16, 2, oracle.prod_row_bytes(128, bits))
+    pages, _, _ = oracle.write_prod(w.rows("k"), np.zeros(shape, np.uint8), w.slots, bits, signs, S)
+    q = w.queries()
+    ref = oracle.paged_prod_scores(q, pages, w.block_table, w.seq_lens, bits, signs, S)
+    bt = w.block_table.copy()
+    bt[0, 3] = -1
+    bt[0, 7] = w.num_blocks
+    bt[1, 0] = w.num_blocks + 100
+    print(f"[qjl] bad block ids: table entries (0,3) -1, (0,7) {w.num_blocks}, (1,0) {w.num_blocks + 100}", flush=True)
+    got = api.prod_scores(ctx, torch.from_numpy(q).cuda(), torch.from_numpy(pages).cuda(),
+                          torch.from_numpy(bt).cuda(), torch.from_numpy(w.seq_lens).cuda(), bits,
+                          torch.from_numpy(S).cuda()).cpu().numpy()
+    want = ref.copy()
+    for b, p in ((0, 3), (0, 7), (1, 0)):
+        want[b, :, 16 * p:16 * (p + 1)] = 0.0
+    tol = 1e-5 * (np.abs(want) + 100.0)
+    assert (np.abs(got - want) <= tol).all()
+    assert not got[0, :, 48:64].any() and not got[0, :, 112:128].any() and not got[1, :, 0:16].any()
+
+
+def test_writer_out_of_range_slots_are_counted_and_skipped(ctx):
+    # slots past the pages raise the error count and write nothing (the
+    # guard page behind the pages stays as it was)
+    bits = 3
+    w = workloads.make_workload("qjlslots", num_q_heads=4, num_kv_heads=2, seq_lens=[40], seed=132)
+    S = torch.from_numpy(workloads.qjl_matrix(128, seed=2)).cuda()
+    RB = oracle.prod_row_bytes(128, bits)
+    guard = torch.full((w.num_blocks + 1, 16, 2, RB), 7, dtype=torch.uint8, device="cuda")
+    pages = guard[:w.num_blocks]
+    slots = torch.from_numpy(w.slots).cuda().clone()
+    slots[5] = w.num_blocks * 16
+    slots[9] = w.num_blocks * 16 + 3
+    print(f"[qjl] out-of-range slots 5 and 9 of {w.num_tokens}", flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.write_kv_prod(ctx, torch.from_numpy(w.rows("k")).cuda(), pages, slots, bits, S, err_count=err,
+                      check_slots=False)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 2
+    assert bool((guard[w.num_blocks] == 7).all())
+    with pytest.raises(api.TQError):
+        api.write_kv_prod(ctx, torch.from_numpy(w.rows("k")).cuda(), pages, slots, bits, S)
