@@ -203,3 +203,27 @@ def test_writer_out_of_range_slots_are_counted_and_skipped(ctx):
     assert bool((guard[w.num_blocks] == 7).all())
     with pytest.raises(api.TQError):
         api.write_kv_prod(ctx, torch.from_numpy(w.rows("k")).cuda(), pages, slots, bits, S)
+
+
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_scores_half_precision_queries(ctx, dt):
+    # fp16 / bf16 queries: the oracle scores the same rounded values
+    bits = 3
+    w = workloads.make_workload("qjlq", num_q_heads=8, num_kv_heads=2, seq_lens=[200, 37], seed=133)
+    S = workloads.qjl_matrix(128, seed=11)
+    signs = oracle.rht_signs(42, 128)
+    shape = (w.num_blocks, 16, 2, oracle.prod_row_bytes(128, bits))
+    pages, _, _ = oracle.write_prod(w.rows("k"), np.zeros(shape, np.uint8), w.slots, bits, signs, S)
+    tq = torch.from_numpy(w.queries()).to(dt)
+    q = tq.float().numpy()
+    print(f"[qjl] scores with {dt} queries", flush=True)
+    ref = oracle.paged_prod_scores(q, pages, w.block_table, w.seq_lens, bits, signs, S)
+    got = api.prod_scores(ctx, tq.cuda(), torch.from_numpy(pages).cuda(), torch.from_numpy(w.block_table).cuda(),
+                          torch.from_numpy(w.seq_lens).cuda(), bits, torch.from_numpy(S).cuda()).cpu().numpy()
+    norms = np.zeros(ref.shape)
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        t = np.arange(L)
+        n = oracle.prod_bytes_to_rows(pages[w.block_table[b, t // 16], t % 16], bits, 128)[1].astype(np.float64)
+        norms[b, :, :L] = np.repeat(n.T, 4, axis=0)
+    _check_scores(got, ref, q, norms, f"scores {dt}")
