@@ -227,3 +227,22 @@ def test_scores_half_precision_queries(ctx, dt):
         n = oracle.prod_bytes_to_rows(pages[w.block_table[b, t // 16], t % 16], bits, 128)[1].astype(np.float64)
         norms[b, :, :L] = np.repeat(n.T, 4, axis=0)
     _check_scores(got, ref, q, norms, f"scores {dt}")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_writer_bf16_rows(ctx, bits):
+    # bf16 raw rows (exact in fp32, which the oracle encodes), slots reversed
+    t = torch.randn(40, 2, 128, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    raw32 = t.float().numpy()
+    slots = np.arange(40, dtype=np.int64)[::-1].copy()
+    S = workloads.qjl_matrix(128, seed=12 + bits)
+    signs = oracle.rht_signs(42, 128)
+    shape = (3, 16, 2, oracle.prod_row_bytes(128, bits))
+    print(f"[qjl] writer bits={bits} bf16 rows", flush=True)
+    ref, near_i, near_s = oracle.write_prod(raw32, np.zeros(shape, np.uint8), slots, bits, signs, S)
+    pg = torch.zeros(shape, dtype=torch.uint8, device="cuda")
+    api.write_kv_prod(ctx, t.cuda(), pg, torch.from_numpy(slots).cuda(), bits, torch.from_numpy(S).cuda())
+    torch.cuda.synchronize()
+    got = pg.cpu().numpy()
+    _compare_rows(got[slots // 16, slots % 16], ref[slots // 16, slots % 16], near_i[slots // 16, slots % 16],
+                  near_s[slots // 16, slots % 16], bits, f"bf16 bits {bits}")
