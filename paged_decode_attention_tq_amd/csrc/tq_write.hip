@@ -294,6 +294,14 @@ __global__ __launch_bounds__(256, 2) void write_prod_kernel(ProdWriteArgs pa) { 
     }
   }
 
+  // lane l < 2^MB holds centroid l of the index codebook (-cpos[HALF - 1 - l]
+  // below HALF, cpos[l - HALF] from HALF); the residual looks it up by index
+  float cent = 0.0f;
+#pragma unroll
+  for (int k = 0; k < HALF; ++k) {
+    cent = (lane & (N - 1)) == HALF + k ? pa.cpos[k] : cent;
+    cent = (lane & (N - 1)) == HALF - 1 - k ? -pa.cpos[k] : cent;
+  }
   const int64_t nblk = (a.num_rows + 63) / 64;
   // the raw slice and slot of this quad's row of block b, requested one
   // block ahead (in flight during the previous block's sketch and stores)
@@ -347,10 +355,7 @@ __global__ __launch_bounds__(256, 2) void write_prod_kernel(ProdWriteArgs pa) { 
       const int pos = MB * j;
       w[pos >> 5] |= idx << (pos & 31);
       if ((pos & 31) + MB > 32) w[(pos >> 5) + 1] |= idx >> (32 - (pos & 31));
-      float cp = pa.cpos[0];
-#pragma unroll
-      for (int k = 1; k < HALF; ++k) cp = cnt == k ? pa.cpos[k] : cp;
-      x[j] = r - (r > 0.0f ? cp : -cp);
+      x[j] = r - __shfl(cent, (int)idx);  // the same fp32 value as r - (+-cpos[cnt])
       ss = fmaf(x[j], x[j], ss);
       mx = fmaxf(mx, __builtin_fabsf(x[j]));
     }
