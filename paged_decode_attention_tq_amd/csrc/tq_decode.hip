@@ -285,6 +285,12 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     }
   }
 
+  // the score MFMAs' B operands (each dword of qd twice), built once so
+  // that the page loop spends no register copies on them
+  half8 Bqs[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) Bqs[m] = __builtin_bit_cast(half8, u32x4{qd[2 * m], qd[2 * m], qd[2 * m + 1], qd[2 * m + 1]});
+
   // ---- lookup tables and block ids -------------------------------------------
   fill_pair_table<KB>(lds + kKTab, a.k_cent, tid, 64 * W);
   if constexpr (!kShareV) fill_pair_table<VB>(lds + kVTab, a.v_cent, tid, 64 * W);
@@ -384,8 +390,7 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
     floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f};
     auto kmfma = [&](int m) {
       const half8 A = __builtin_bit_cast(half8, u32x4{kh[2 * m], kl[2 * m], kh[2 * m + 1], kl[2 * m + 1]});
-      const half8 Bq = __builtin_bit_cast(half8, u32x4{qd[2 * m], qd[2 * m], qd[2 * m + 1], qd[2 * m + 1]});
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bq, sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bqs[m], sc, 0, 0, 0);
     };
     // rolling window: the lookups of the next two MFMAs are in flight while
     // one runs, which keeps few lookup results live at a time
