@@ -421,8 +421,9 @@ def main():
     ap.add_argument("--no-stream-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush (1 GiB write, then 1 GiB read) before each timed step")
-    ap.add_argument("--op", choices=("decode", "decompress", "hybrid", "prefill", "prod"), default="decode",
-                    help="decode: the decode step (default); decompress: the dense readback of every K row; "
+    ap.add_argument("--op", choices=("decode", "append", "decompress", "hybrid", "prefill", "prod"), default="decode",
+                    help="decode: the decode step (default); append: the same step as one call that writes the new "
+                         "rows inside the decode (tq_paged_decode_append); decompress: the dense readback of every K row; "
                          "hybrid: the decode step over the packed pages plus an exact fp16 window per sequence; "
                          "prefill: a chunk of --q-len queries per sequence attending causally over the pages; "
                          "prod: the prod key codec (writer of every K row, then every head's scores over them)")
@@ -501,6 +502,7 @@ def main():
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     hybrid = args.op == "hybrid"
     prefill = args.op == "prefill"
+    append = args.op == "append"
     if prefill:
         # the last q_len tokens of every sequence query the pages (their rows are
         # rewritten each step like the decode step's new token)
@@ -539,10 +541,16 @@ def main():
             flush_rd.sum()
         if i is not None:
             ev[i][0].record()
-        api.write_kv_pair(ctx, k_new, v_new, kp, vp, new_slots, w.k_bits, w.v_bits, err_count=err, check_slots=False)
+        if not append:
+            api.write_kv_pair(ctx, k_new, v_new, kp, vp, new_slots, w.k_bits, w.v_bits, err_count=err,
+                              check_slots=False)
         if i is not None:
             ev[i][1].record()
-        if prefill:
+        if append:  # the new rows are written by the decode kernel itself
+            api.paged_decode_append(ctx, q_d, k_new, v_new, kp, vp, bt, lens, w.k_bits, w.v_bits,
+                                    max_seq_len=w.max_seq_len, out=out, workspace=ws, err_count=err,
+                                    check_pages=False)
+        elif prefill:
             api.paged_prefill(ctx, pq, ql_d, kp, vp, bt, lens, w.k_bits, w.v_bits, max_seq_len=w.max_seq_len,
                               out=out, workspace=ws)
         elif hybrid:
@@ -578,8 +586,10 @@ def main():
     dec_s = float(dec_ms.mean()) / 1e3
     achieved = packed / dec_s / 1e9
     result = {
-        "metric": ("paged TQ decode tokens/s + packed-KV HBM GB/s (% of peak), 1 MI355X" if not (hybrid or prefill)
-                   else f"paged TQ hybrid decode (packed history + {args.window}-row exact fp16 window) tokens/s + "
+        "metric": ("paged TQ decode tokens/s + packed-KV HBM GB/s (% of peak), 1 MI355X" if not (hybrid or prefill
+                                                                                            or append)
+                   else "paged TQ decode step as one call (new rows written by the decode) tokens/s + packed-KV HBM "
+                   "GB/s (% of peak), 1 MI355X" if append else f"paged TQ hybrid decode (packed history + {args.window}-row exact fp16 window) tokens/s + "
                    "HBM GB/s (% of peak), 1 MI355X" if hybrid else
                    f"paged TQ multi-query attention ({args.q_len} causal queries per sequence) query tokens/s + "
                    "packed-KV HBM GB/s (% of peak), 1 MI355X"),
@@ -613,8 +623,10 @@ def main():
         "context_tokens_per_s": float(w.num_tokens) / dec_s,
         "roofline": {
             "bound": "hbm",
-            "kernel": ((f"tq_paged_decode, {kernel} decode kernel + merge kernel" if kernel != "wave1" else
-                        "tq_paged_decode, wave decode kernel as one workgroup (no merge kernel)") +
+            "kernel": (("tq_paged_decode_append" if append else "tq_paged_decode") +
+                       (f", {kernel} decode kernel + merge kernel" if kernel != "wave1" else
+                        ", wave decode kernel as one workgroup (no merge kernel)") +
+                       (" (the new rows encoded inside the decode kernel)" if append else "") +
                        (" + hybrid_window_kernel" if hybrid else "") +
                        (" + layout, tail readback and causal window kernels" if prefill else "")),
             "achieved": achieved,
@@ -622,7 +634,8 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": (op_traffic_bytes("hybrid", f"{w.name}/window{args.window}") if hybrid else
-                        op_traffic_bytes("prefill", f"{w.name}/q{args.q_len}") if prefill else traffic_bytes(w.name)),
+                        op_traffic_bytes("prefill", f"{w.name}/q{args.q_len}") if prefill else
+                        op_traffic_bytes("append", w.name) if append else traffic_bytes(w.name)),
         },
         "prefill_write": write,
         "stream_read_ceiling": None,

@@ -274,6 +274,42 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype,
                           float* out, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* One decode step in one call: the new token's K and V rows are written into
+ * the pages and the decode attends over every token including it
+ * ("Architecture", "Cache Lifecycle": a decoded token's KV joins the cache
+ * before the next step attends; rows as in "vLLM Usage", "TQ Byte Layout").
+ * For each sequence b with L_b = min(seq_lens[b], the decode's clamp) > 0,
+ * k_new[b] and v_new[b] are encoded exactly as tq_write_kv encodes them and
+ * stored at token L_b - 1, i.e. row (L_b - 1) % block_size of page
+ * block_table[b, (L_b - 1) / block_size]; then the result is tq_paged_decode's
+ * over tokens 0 .. L_b - 1.  Output and pages are bit for bit those of
+ * tq_write_kv_pair at those slots followed by tq_paged_decode.  Where
+ * tq_decode_kernel() names "staged", the decode kernel writes the rows itself
+ * (the workgroup that reads the page stores them first), so a step is one
+ * decode launch (plus the split merge) instead of a write launch and a decode
+ * launch; for the wave kernels a writer launch that finds the slots on the
+ * device from seq_lens and block_table runs first.
+ *   q ... k_bits, v_pages ... workspace, workspace_bytes: as tq_paged_decode
+ *     (k_pages and v_pages are written, at those rows only).
+ *   k_new, v_new  device, [batch, num_kv_heads, head_dim] of new_dtype (fp32,
+ *                 fp16 or bf16), contiguous, 4-byte aligned.
+ *   err_count     device int32 or NULL: incremented once per sequence whose
+ *                 last page's block id lies outside [0, num_blocks); that
+ *                 sequence's rows are not written (and the page reads as
+ *                 zero rows, as in tq_paged_decode).
+ * Same support, errors and asynchrony as tq_paged_decode; the pages must not
+ * be read or written by other work while the call runs. */
+tq_status tq_paged_decode_append(const tq_ctx* ctx, const void* q, tq_dtype q_dtype,
+                                 int batch, int num_q_heads, int num_kv_heads,
+                                 const void* k_new, const void* v_new, tq_dtype new_dtype,
+                                 uint8_t* k_pages, int k_bits,
+                                 uint8_t* v_pages, int v_bits,
+                                 int64_t num_blocks, int block_size,
+                                 const int32_t* block_table, int max_blocks_per_seq,
+                                 const int32_t* seq_lens, int max_seq_len, float scale,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 int32_t* err_count, void* stream);
+
 /* Bytes of device workspace tq_paged_decode_hybrid needs: the decode's
  * workspace (rounded up to 256 bytes) plus one float per query head for the
  * packed part's log-sum-exp.  Same arguments, rules and device dependence as

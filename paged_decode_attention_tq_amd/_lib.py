@@ -72,6 +72,14 @@ SIGNATURES = {
          _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_float,
          _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p],
     ),
+    "tq_paged_decode_append": (
+        _c.c_int,
+        [_c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+         _c.c_void_p, _c.c_void_p, _c.c_int,
+         _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int,
+         _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_float,
+         _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p, _c.c_void_p],
+    ),
     "tq_hybrid_workspace_bytes": (
         _c.c_size_t, [_c.c_void_p, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
     "tq_paged_decode_hybrid": (

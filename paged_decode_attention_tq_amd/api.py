@@ -35,6 +35,7 @@ __all__ = [
     "prefill_workspace_bytes",
     "paged_prefill",
     "paged_decode_noalloc",
+    "paged_decode_append",
 ]
 
 _DTYPES = {torch.float32: _lib.TQ_F32, torch.float16: _lib.TQ_F16, torch.bfloat16: _lib.TQ_BF16}
@@ -308,6 +309,61 @@ def paged_decode(ctx: Context, q: torch.Tensor, k_pages: torch.Tensor, v_pages: 
         seq_lens.data_ptr(), max_seq_len, float(scale) if scale else 0.0, out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q))
     check(st, "tq_paged_decode")
+    return out
+
+
+def paged_decode_append(ctx: Context, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                        seq_lens: torch.Tensor, k_bits: int, v_bits: int, max_seq_len: int | None = None,
+                        scale: float | None = None, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, err_count: torch.Tensor | None = None,
+                        check_pages: bool = True) -> torch.Tensor:
+    """One decode step in one call: the new rows ``k_new``/``v_new`` ``[B, Hkv, d]``
+    are written at each sequence's last token (position ``seq_lens[b] - 1``)
+    and the decode attends over every token -> fp32 ``[B, Hq, d]``.
+
+    Equal bit for bit to ``write_kv_pair`` at those slots followed by
+    ``paged_decode``.  A sequence whose last page has a block id outside the
+    pages is counted in ``err_count`` and its rows are not written; with
+    ``check_pages`` the call synchronises and raises ``TQError`` if any were.
+    """
+    _need(q.is_cuda and q.dim() == 3 and q.shape[2] == ctx.head_dim and q.is_contiguous(), "q must be [B, Hq, d]")
+    _need(q.dtype in _DTYPES, "q dtype must be fp32/fp16/bf16")
+    B, Hq, d = q.shape
+    for name, pg, bits in (("k_pages", k_pages, k_bits), ("v_pages", v_pages, v_bits)):
+        _need(pg.dtype == torch.uint8 and pg.dim() == 4 and pg.is_contiguous(), f"{name} must be uint8 4-D")
+        _need(pg.shape[3] == row_bytes(d, bits), f"{name} row_bytes does not match bits")
+    NB, BS, Hkv, _ = k_pages.shape
+    _need(tuple(v_pages.shape[:3]) == (NB, BS, Hkv), "k_pages / v_pages geometry mismatch")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t.is_cuda and t.shape == (B, Hkv, d) and t.is_contiguous(), f"{name} must be [B, Hkv, d]")
+    _need(k_new.dtype == v_new.dtype and k_new.dtype in _DTYPES, "k_new / v_new must share an fp32/fp16/bf16 dtype")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.shape[0] == B
+          and block_table.is_contiguous(), "block_table must be int32 [B, max_blocks]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.shape == (B,), "seq_lens must be int32 [B]")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out.dtype == torch.float32 and out.shape == (B, Hq, d) and out.is_contiguous(), "out must be fp32 [B, Hq, d]")
+    need = decode_workspace_bytes(ctx, B, Hq, Hkv, max_seq_len, BS)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    own = err_count is None and check_pages
+    if own:
+        err_count = torch.zeros(1, dtype=torch.int32, device=q.device)
+    st = _lib.lib().tq_paged_decode_append(
+        ctx.handle, q.data_ptr(), _DTYPES[q.dtype], B, Hq, Hkv, k_new.data_ptr(), v_new.data_ptr(),
+        _DTYPES[k_new.dtype], k_pages.data_ptr(), k_bits, v_pages.data_ptr(), v_bits, NB, BS,
+        block_table.data_ptr(), block_table.shape[1], seq_lens.data_ptr(), max_seq_len,
+        float(scale) if scale else 0.0, out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), err_count.data_ptr() if err_count is not None else None,
+        _stream(q))
+    check(st, "tq_paged_decode_append")
+    if check_pages:
+        n_bad = int(err_count.item())
+        if n_bad:
+            raise TQError(f"tq_paged_decode_append: {n_bad} sequence(s) whose last page is outside the pages")
     return out
 
 

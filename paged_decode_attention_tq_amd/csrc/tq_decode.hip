@@ -38,6 +38,7 @@
 // distinct banks).
 
 #include "tq_decode_common.h"
+#include "tq_encode.h"
 
 #include <type_traits>
 #include <utility>
@@ -54,7 +55,7 @@ constexpr int kWgThreads = 64 * kMaxWaves;
 // contiguous bytes it is; else per-token chunk windows over the slice of the
 // workgroup's heads.  MAXLD: 1 KB loads per wave per stage.
 
-template <int KB, int VB, bool CONTIG, int MAXLD>
+template <int KB, int VB, bool CONTIG, int MAXLD, bool APP>
 __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) {
   // all of the CU's LDS, statically: addresses are then known constants
   __shared__ __attribute__((aligned(16))) uint8_t lds[kDecodeLdsBytes];
@@ -85,6 +86,36 @@ __global__ __launch_bounds__(kWgThreads) void decode_split_kernel(DecodeArgs a) 
   const int p0 = s * a.pages_per_split;
   if (p0 >= npages) return;  // the whole workgroup leaves together
   const int span = min(a.pages_per_split, npages - p0);
+
+  // ---- appending decode: the new row of the sequence ------------------------------
+  // The workgroup holding the sequence's last page (the last split; one per
+  // group of KV heads) encodes its heads' K and V rows of the last token as
+  // the row writer does and stores them into that page, first thing, while
+  // few registers are live.  The prologue barrier orders the stores before
+  // every page copy of the workgroup, and no other workgroup reads the page.
+  // Quad r < 2 kv_per_wg (kv_per_wg <= waves, 16 quads each) takes component
+  // r / kv_per_wg of head kv_per_wg hg + r % kv_per_wg.
+  if (APP && s == (npages - 1) / a.pages_per_split) {
+    const int tid0 = __builtin_amdgcn_workitem_id_x();
+    const int blk = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)b * a.max_blocks_per_seq + (L - 1) / kBlockSize]);
+    const bool ok = blk >= 0 && (int64_t)blk < a.num_blocks;
+    const int r = tid0 >> 2;
+    if (ok && r < 2 * a.kv_per_wg) {
+      const int comp = r / a.kv_per_wg;
+      const int head = a.kv_per_wg * hg + (r - comp * a.kv_per_wg);
+      const int64_t elem = ((int64_t)b * a.num_kv_heads + head) * kHeadDim;
+      const int64_t tok_row = (int64_t)((L - 1) % kBlockSize) * a.num_kv_heads + head;
+      if (comp == 0)
+        load_encode_store_row<KB>(a.app.k_new, a.app.new_dtype, elem, tid0 & 3, a.sign_bits, a.app.k_bounds,
+                                  const_cast<uint8_t*>(a.k_pages) + (int64_t)blk * a.k_page_bytes + tok_row * a.k_row_bytes,
+                                  a.k_row_bytes);
+      else
+        load_encode_store_row<VB>(a.app.v_new, a.app.new_dtype, elem, tid0 & 3, a.sign_bits, a.app.v_bounds,
+                                  const_cast<uint8_t*>(a.v_pages) + (int64_t)blk * a.v_page_bytes + tok_row * a.v_row_bytes,
+                                  a.v_row_bytes);
+    }
+    if (!ok && tid0 == 0 && hg == 0 && a.app.err_count) atomicAdd(a.app.err_count, 1);
+  }
 
   // the wave index is uniform; say so, so that everything derived from it
   // (head, page stream, load assignment) lives in scalar registers
@@ -666,7 +697,14 @@ int decode_merge_lds_bytes() { return kMaxWaves * 8 * (kHeadDim + 2) * 4; }
 template <int KB, int VB, bool CONTIG, int MAXLD>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const long long units = (long long)a.batch * a.head_groups * a.num_splits;
-  hipLaunchKernelGGL((decode_split_kernel<KB, VB, CONTIG, MAXLD>), dim3((unsigned)units), dim3(64 * a.waves), 0, st, a);
+  // the appending decode is its own instantiation, so that the plain decode
+  // compiles without the row encode
+  if (a.app.on)
+    hipLaunchKernelGGL((decode_split_kernel<KB, VB, CONTIG, MAXLD, true>), dim3((unsigned)units), dim3(64 * a.waves), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<KB, VB, CONTIG, MAXLD, false>), dim3((unsigned)units), dim3(64 * a.waves),
+                       0, st, a);
   return hipGetLastError();
 }
 

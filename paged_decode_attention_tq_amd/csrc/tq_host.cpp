@@ -692,7 +692,8 @@ tq_status decode_impl(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int ba
                       int num_kv_heads, const uint8_t* k_pages, int k_bits, const uint8_t* v_pages, int v_bits,
                       int64_t num_blocks, int block_size, const int32_t* block_table, int max_blocks_per_seq,
                       const int32_t* seq_lens, int max_seq_len, float scale, float* out, float* lse_out,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      const tq::AppendArgs* app = nullptr) {
   if (!ctx || batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_seq_len < 0)
     return TQ_ERR_INVALID_ARG;
@@ -751,6 +752,30 @@ tq_status decode_impl(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int ba
     std::memcpy(w.sign_bits, ctx->sign_bits, sizeof(w.sign_bits));
     for (int j = 0; j < (1 << k_bits); ++j) w.k_cent[j] = ctx->cent[k_bits][j] * k_scale;
     for (int j = 0; j < (1 << v_bits); ++j) w.v_cent[j] = ctx->cent[v_bits][j] * v_scale;
+    if (app) {
+      // the wave-private decode does not append: the appending row writer
+      // runs first (a workgroup that also encoded would hold every later
+      // page load of its sequences' ends behind the encode)
+      tq::AppendWriteArgs aw;
+      std::memset(&aw, 0, sizeof(aw));
+      aw.app = *app;
+      aw.k_pages = const_cast<uint8_t*>(k_pages);
+      aw.v_pages = const_cast<uint8_t*>(v_pages);
+      aw.block_table = block_table;
+      aw.seq_lens = seq_lens;
+      aw.k_page_bytes = w.k_page_bytes;
+      aw.v_page_bytes = w.v_page_bytes;
+      aw.num_blocks = num_blocks;
+      aw.batch = batch;
+      aw.num_kv_heads = num_kv_heads;
+      aw.max_blocks_per_seq = max_blocks_per_seq;
+      aw.max_len = w.max_len;
+      aw.k_row_bytes = k_row_bytes;
+      aw.v_row_bytes = v_row_bytes;
+      std::memcpy(aw.sign_bits, ctx->sign_bits, sizeof(aw.sign_bits));
+      const tq_status sa = hip_status(tq::launch_write_append(aw, k_bits, v_bits, (hipStream_t)stream));
+      if (sa != TQ_OK) return sa;
+    }
     tq_status st = hip_status(tq::launch_decode_wave(w, k_bits, v_bits, wp.nh, (hipStream_t)stream));
     if (st != TQ_OK || w.direct) return st;
     tq::WaveMergeArgs m;
@@ -823,6 +848,7 @@ tq_status decode_impl(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int ba
   std::memcpy(d.sign_bits, ctx->sign_bits, sizeof(d.sign_bits));
   for (int j = 0; j < (1 << k_bits); ++j) d.k_cent[j] = ctx->cent[k_bits][j] * k_scale;
   for (int j = 0; j < (1 << v_bits); ++j) d.v_cent[j] = ctx->cent[v_bits][j] * v_scale;
+  if (app) d.app = *app;
   // per-page byte offsets are 32-bit inside a page
   if (d.k_page_bytes > (1 << 30) || d.v_page_bytes > (1 << 30)) return TQ_ERR_UNSUPPORTED;
 
@@ -859,6 +885,32 @@ tq_status tq_paged_decode(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, in
   return decode_impl(ctx, q, q_dtype, batch, num_q_heads, num_kv_heads, k_pages, k_bits, v_pages, v_bits,
                      num_blocks, block_size, block_table, max_blocks_per_seq, seq_lens, max_seq_len, scale, out,
                      nullptr, workspace, workspace_bytes, stream);
+}
+
+tq_status tq_paged_decode_append(const tq_ctx* ctx, const void* q, tq_dtype q_dtype, int batch,
+                                 int num_q_heads, int num_kv_heads, const void* k_new, const void* v_new,
+                                 tq_dtype new_dtype, uint8_t* k_pages, int k_bits, uint8_t* v_pages, int v_bits,
+                                 int64_t num_blocks, int block_size, const int32_t* block_table,
+                                 int max_blocks_per_seq, const int32_t* seq_lens, int max_seq_len, float scale,
+                                 float* out, void* workspace, size_t workspace_bytes, int32_t* err_count,
+                                 void* stream) {
+  if (new_dtype != TQ_F32 && new_dtype != TQ_F16 && new_dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+  if (!ctx || !bits_ok(k_bits) || !bits_ok(v_bits)) return ctx ? TQ_ERR_UNSUPPORTED : TQ_ERR_INVALID_ARG;
+  if (batch > 0 && (!k_new || !v_new)) return TQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k_new) & 3) || (reinterpret_cast<uintptr_t>(v_new) & 3)) return TQ_ERR_ALIGNMENT;
+  tq::AppendArgs app;
+  std::memset(&app, 0, sizeof(app));
+  app.k_new = k_new;
+  app.v_new = v_new;
+  app.err_count = err_count;
+  app.on = 1;
+  app.new_dtype = (int)new_dtype;
+  const int nk = 1 << k_bits, nv = 1 << v_bits;
+  for (int j = 0; j < nk / 2 - 1; ++j) app.k_bounds[j] = ctx->bound[k_bits][nk / 2 + j];
+  for (int j = 0; j < nv / 2 - 1; ++j) app.v_bounds[j] = ctx->bound[v_bits][nv / 2 + j];
+  return decode_impl(ctx, q, q_dtype, batch, num_q_heads, num_kv_heads, k_pages, k_bits, v_pages, v_bits,
+                     num_blocks, block_size, block_table, max_blocks_per_seq, seq_lens, max_seq_len, scale, out,
+                     nullptr, workspace, workspace_bytes, stream, &app);
 }
 
 size_t tq_hybrid_workspace_bytes(const tq_ctx* ctx, int batch, int num_q_heads, int num_kv_heads,

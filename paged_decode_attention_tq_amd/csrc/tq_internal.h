@@ -87,6 +87,46 @@ struct ReadArgs {
   uint32_t neg_bits[4];
 };
 
+// The new row of every sequence appended by the decode itself
+// (tq_paged_decode_append): the K and V rows of sequence b's last token
+// (position L_b - 1, L_b its clamped length) are encoded as the row writer
+// encodes them and stored in that token's page, by the staged decode's
+// workgroup that reads the page before any of its waves reads it, or by the
+// appending row writer ahead of the wave-private decode.  on == 0: nothing
+// is written.
+struct AppendArgs {
+  const void* k_new;             // [B, Hkv, 128] of new_dtype
+  const void* v_new;
+  int32_t* err_count;            // nullable: sequences whose last page has a block id outside the pages
+  int32_t on;
+  int32_t new_dtype;             // tq_dtype of k_new and v_new
+  float k_bounds[16];            // the 2^(b_k - 1) - 1 positive boundaries of the K codebook, increasing
+  float v_bounds[16];
+};
+
+// Arguments of the appending row writer (tq_write.hip), used where the decode
+// kernel does not append the rows itself: row r = 2 (b Hkv + head) + comp of
+// the launch encodes component comp (0 K, 1 V) of sequence b's new row for
+// head `head` at its last token, found on the device from seq_lens and the
+// block table exactly as the decode finds it.
+struct AppendWriteArgs {
+  AppendArgs app;
+  uint8_t* k_pages;
+  uint8_t* v_pages;
+  const int32_t* block_table;    // [B, max_blocks_per_seq]
+  const int32_t* seq_lens;       // [B]
+  int64_t k_page_bytes;
+  int64_t v_page_bytes;
+  int64_t num_blocks;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t max_len;               // lengths are clamped to this, as by the decode
+  int32_t k_row_bytes;
+  int32_t v_row_bytes;
+  uint32_t sign_bits[kHeadDim / 32];
+};
+
 // Arguments of the decode split kernel.  One workgroup handles one
 // (sequence, group of kv_per_wg KV heads, split of pages_per_split pages)
 // with waves = kv_per_wg * q_groups * streams waves: each wave owns one KV
@@ -135,6 +175,7 @@ struct DecodeArgs {
   uint32_t sign_bits[kHeadDim / 32];
   float k_cent[32];              // fp32 centroids of K times k_scale
   float v_cent[32];              // fp32 centroids of V times v_scale
+  AppendArgs app;
 };
 
 // Arguments of the wave-private decode kernel (tq_decode_wave.hip).  The
@@ -262,6 +303,8 @@ hipError_t launch_write(const WriteArgs& a, int raw_dtype, int bits, hipStream_t
 // prod key rows of `bits` bits (2..5): indices at bits - 1, sketch signs, gamma
 hipError_t launch_write_prod(const ProdWriteArgs& a, int raw_dtype, int bits, int num_cus, hipStream_t stream);
 hipError_t launch_prod_scores(const ProdScoreArgs& a, int bits, hipStream_t stream);
+// the new row of every sequence at its last token (AppendWriteArgs)
+hipError_t launch_write_append(const AppendWriteArgs& a, int k_bits, int v_bits, hipStream_t stream);
 // K and V rows of the same tokens (same num_rows) in one launch
 hipError_t launch_write_pair(const WriteArgs& k, const WriteArgs& v, int raw_dtype, int k_bits, int v_bits,
                              hipStream_t stream);

@@ -7,55 +7,16 @@
 // ignored, out-of-range slots are an error); pages: "Architecture" section
 // "Cache Storage Objects" ([num_blocks, block_size, num_kv_heads, row_bytes]).
 
-#include "tq_internal.h"
-#include "tq_device.h"
+#include "tq_encode.h"
 
 #include <algorithm>
 
 namespace tq {
 
 // ==========================================================================
-// Row writer: one row (token, head) per 4-lane quad, 32 elements per lane.
-//
-// Per row: n = fp32(sqrt(sum x^2)) with the sum exact-rounded in float64
-// (fast path: plain float64 accumulation; when the error bound does not
-// decide the fp32 rounding, the row is re-summed with double-double
-// arithmetic); r = H (s * x) / (n sqrt(128)); idx = nearest centroid via the
-// symmetric boundary count; LSB-first pack; store at the slot.
+// Row writer: one row (token, head) per 4-lane quad, 32 elements per lane,
+// encoded as tq_encode.h describes and stored at the row's slot.
 // ==========================================================================
-
-template <int DT>
-__device__ __forceinline__ void load_row32(const void* raw, int64_t elem_off, float (&x)[32]) {
-  if constexpr (DT == 0) {  // fp32: 8 x 16 bytes
-    const float* p = static_cast<const float*>(raw) + elem_off;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(p + 4 * i);
-      x[4 * i + 0] = __uint_as_float(v.x);
-      x[4 * i + 1] = __uint_as_float(v.y);
-      x[4 * i + 2] = __uint_as_float(v.z);
-      x[4 * i + 3] = __uint_as_float(v.w);
-    }
-  } else {  // fp16 / bf16: 4 x 16 bytes
-    const uint16_t* p = static_cast<const uint16_t*>(raw) + elem_off;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(p + 8 * i);
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint16_t lo = (uint16_t)(w[k] & 0xFFFF), hi = (uint16_t)(w[k] >> 16);
-        if constexpr (DT == 1) {
-          x[8 * i + 2 * k] = (float)__builtin_bit_cast(_Float16, lo);
-          x[8 * i + 2 * k + 1] = (float)__builtin_bit_cast(_Float16, hi);
-        } else {
-          x[8 * i + 2 * k] = bf16_to_f32(lo);
-          x[8 * i + 2 * k + 1] = bf16_to_f32(hi);
-        }
-      }
-    }
-  }
-}
 
 // The same row slice as raw words: loads issued now, widened later.
 template <int DT>
@@ -90,80 +51,9 @@ __device__ __forceinline__ void widen_raw(const RawSlice<DT>& r, float (&x)[32])
   }
 }
 
-// n = fp32(sqrt(sum x^2)) of the quad's row, the sum exact-rounded in
-// float64: the fast sum has relative error below 40 * 2^-53 (the sqrt halves
-// it); when that bound does not decide the fp32 rounding, the row is re-summed
-// with double-double arithmetic.  Returns the float64 root.
-__device__ __forceinline__ double row_norm(const float (&x)[32]) {
-  double s = 0.0;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) s = __builtin_fma((double)x[j], (double)x[j], s);
-  s += quad_xor<1>(s);
-  s += quad_xor<2>(s);
-  double n64 = sqrt_rn(s);
-  const double lo = n64 * (1.0 - 0x1p-47), hi = n64 * (1.0 + 0x1p-47);
-  if ((float)lo != (float)hi) {
-    double sh = 0.0, sl = 0.0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      double sq = (double)x[j] * (double)x[j];  // exact
-      double t, e;
-      two_sum(sh, sq, t, e);
-      sh = t;
-      sl += e;
-    }
-    {
-      double oh = quad_xor<1>(sh), ol = quad_xor<1>(sl), t, e;
-      two_sum(sh, oh, t, e);
-      sh = t;
-      sl = sl + ol + e;
-    }
-    {
-      double oh = quad_xor<2>(sh), ol = quad_xor<2>(sl), t, e;
-      two_sum(sh, oh, t, e);
-      sh = t;
-      sl = sl + ol + e;
-    }
-    n64 = sqrt_rn(sh + sl);
-  }
-  return n64;
-}
-
-// x <- H (s * x) over the quad's 128 coordinates (lane q holds 32q .. 32q + 31):
-// the sign flip, five butterfly stages in the lane, two across the quad.
-__device__ __forceinline__ void rotate_row(const uint32_t* sign_bits, int q, float (&x)[32]) {
-  uint32_t sw = pick4(sign_bits, q);
-  asm volatile("" : "+v"(sw));  // one register, not 32 sign masks hoisted out of a caller's loop
-#pragma unroll
-  for (int j = 0; j < 32; ++j) x[j] = __uint_as_float(__float_as_uint(x[j]) ^ (((sw >> j) & 1u) << 31));
-#pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if ((j & h) == 0) {
-        const float u = x[j], v = x[j + h];
-        x[j] = u + v;
-        x[j + h] = u - v;
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float p = quad_xor<1>(x[j]);
-    x[j] = (q & 1) ? p - x[j] : x[j] + p;
-  }
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float p = quad_xor<2>(x[j]);
-    x[j] = (q & 2) ? p - x[j] : x[j] + p;
-  }
-}
-
 // The rows of workgroup `wg` (64 rows, one per 4-lane quad) of one call.
 template <int BITS, int DT>
 __device__ __forceinline__ void write_rows(const WriteArgs& a, int64_t wg) {
-  constexpr int N = 1 << BITS;
-  constexpr int HALF = N / 2;
   const int q = threadIdx.x & 3;
   const int64_t row = wg * 64 + (threadIdx.x >> 2);
   if (row >= a.num_rows) return;  // uniform per quad
@@ -180,34 +70,9 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, int64_t wg) {
     return;
   }
 
-  const double n64 = row_norm(x);
-  const float n32 = (float)n64;
-  const float c = n64 > 0.0 ? (float)(1.0 / (n64 * 11.313708498984761)) : 0.0f;  // 1/(n sqrt(128))
-  rotate_row(a.sign_bits, q, x);
-
-  // ---- nearest centroid and LSB-first packing ----------------------------
-  uint32_t w[BITS];
-#pragma unroll
-  for (int k = 0; k < BITS; ++k) w[k] = 0;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float r = x[j] * c;
-    const float ar = __builtin_fabsf(r);
-    int cnt = 0;
-#pragma unroll
-    for (int k = 0; k < HALF - 1; ++k) cnt += (ar > a.pos_bounds[k]) ? 1 : 0;
-    const uint32_t idx = (uint32_t)(r > 0.0f ? HALF + cnt : HALF - 1 - cnt);
-    const int pos = BITS * j;
-    w[pos >> 5] |= idx << (pos & 31);
-    if ((pos & 31) + BITS > 32) w[(pos >> 5) + 1] |= idx >> (32 - (pos & 31));
-  }
-
   uint8_t* dst = a.pages + (slot / a.block_size) * a.page_bytes +
                  ((slot % a.block_size) * a.num_kv_heads + head) * (int64_t)a.row_bytes;
-  uint32_t* d32 = reinterpret_cast<uint32_t*>(dst) + BITS * q;
-#pragma unroll
-  for (int k = 0; k < BITS; ++k) d32[k] = w[k];
-  if (q == 3) *reinterpret_cast<float*>(dst + a.row_bytes - 4) = n32;
+  encode_store_row<BITS>(x, q, a.sign_bits, a.pos_bounds, dst, a.row_bytes);
 }
 
 template <int BITS, int DT>
@@ -224,6 +89,66 @@ __global__ __launch_bounds__(256) void write_pair_kernel(WriteArgs k, WriteArgs 
     write_rows<KB, DT>(k, wg);
   else
     write_rows<VB, DT>(v, wg - k_groups);
+}
+
+// ==========================================================================
+// Appending row writer: one row per quad, row r = 2 (b Hkv + head) + comp.
+// The last token of sequence b is L_b - 1 (L_b its length clamped to
+// 0 .. max_len); an empty sequence has no new row, and a last page whose
+// block id lies outside the pages is counted once (by its K row of head 0)
+// and not written.
+// ==========================================================================
+template <int KB, int VB>
+__global__ __launch_bounds__(256) void write_append_kernel(AppendWriteArgs a) {
+  const int q = threadIdx.x & 3;
+  const int64_t r = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+  if (r >= 2LL * a.batch * a.num_kv_heads) return;  // uniform per quad
+  const int comp = (int)(r & 1);
+  const int64_t bh = r >> 1;
+  const int b = (int)(bh / a.num_kv_heads);
+  const int head = (int)(bh - (int64_t)b * a.num_kv_heads);
+  // the raw row and the length are read together; the block id follows
+  float x[32];
+  load_row_any(comp == 0 ? a.app.k_new : a.app.v_new, a.app.new_dtype, bh * kHeadDim + 32 * q, x);
+  const int L = min(max(a.seq_lens[b], 0), a.max_len);
+  if (L <= 0) return;
+  const int blk = a.block_table[(int64_t)b * a.max_blocks_per_seq + (L - 1) / kBlockSize];
+  if (blk < 0 || (int64_t)blk >= a.num_blocks) {
+    if (comp == 0 && head == 0 && q == 0 && a.app.err_count) atomicAdd(a.app.err_count, 1);
+    return;
+  }
+  const int64_t tok_row = (int64_t)((L - 1) % kBlockSize) * a.num_kv_heads + head;
+  if (comp == 0)
+    encode_store_row<KB>(x, q, a.sign_bits, a.app.k_bounds,
+                         a.k_pages + (int64_t)blk * a.k_page_bytes + tok_row * a.k_row_bytes, a.k_row_bytes);
+  else
+    encode_store_row<VB>(x, q, a.sign_bits, a.app.v_bounds,
+                         a.v_pages + (int64_t)blk * a.v_page_bytes + tok_row * a.v_row_bytes, a.v_row_bytes);
+}
+
+template <int KB>
+static hipError_t launch_write_append_k(const AppendWriteArgs& a, int v_bits, dim3 grid, hipStream_t st) {
+  switch (v_bits) {
+    case 2: hipLaunchKernelGGL((write_append_kernel<KB, 2>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((write_append_kernel<KB, 3>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((write_append_kernel<KB, 4>), grid, dim3(256), 0, st, a); break;
+    case 5: hipLaunchKernelGGL((write_append_kernel<KB, 5>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_write_append(const AppendWriteArgs& a, int k_bits, int v_bits, hipStream_t stream) {
+  const long long rows = 2LL * a.batch * a.num_kv_heads;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 63) / 64));
+  switch (k_bits) {
+    case 2: return launch_write_append_k<2>(a, v_bits, grid, stream);
+    case 3: return launch_write_append_k<3>(a, v_bits, grid, stream);
+    case 4: return launch_write_append_k<4>(a, v_bits, grid, stream);
+    case 5: return launch_write_append_k<5>(a, v_bits, grid, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 // ==========================================================================
