@@ -1,8 +1,8 @@
 """The library's calls inside a captured HIP graph.
 
-The library never allocates and never synchronises inside tq_write_kv_pair
-and tq_paged_decode (the caller owns out, the workspace and err_count), so a
-decode step can be captured once and replayed ("vLLM Usage", Live Backend
+The library never allocates and never synchronises inside tq_write_kv_pair,
+tq_paged_decode and tq_paged_decode_append (the caller owns out, the
+workspace and err_count), so a decode step can be captured once and replayed ("vLLM Usage", Live Backend
 Gap: graph buffer ownership).  The graph holds only the library's kernels: the
 error counter is zeroed before the capture, so no memset is recorded.  Every
 replay, with eager work and synchronisations between replays, must give the
@@ -188,5 +188,62 @@ def test_graph_prod_codec(ctx):
         torch.cuda.synchronize()
         for got, want in zip((pages, scores), eager):
             assert torch.equal(got, want), f"replay {r} differs from the eager call"
+        del junk
+    assert int(err.item()) == 0
+
+
+# the one-call decode step: the staged kernel's appending instantiation, and a
+# wave-kernel shape (writer launch, then the decode and its merge)
+@pytest.mark.parametrize("hkv,G,lens", [(8, 8, [700, 33, 1500]), (2, 8, [700, 33, 0])])
+def test_graph_append_step(ctx, hkv, G, lens):
+    w = workloads.make_workload(f"grapp{hkv}", num_q_heads=hkv * G, num_kv_heads=hkv, seq_lens=lens, seed=60 + hkv)
+    kernel = api.decode_kernel(w.batch, w.num_q_heads, hkv, w.max_seq_len, 4, 4)
+    print(f"[graph] append Hkv={hkv} G={G} lens={w.seq_lens.tolist()} kernel={kernel}", flush=True)
+    dev = torch.device("cuda")
+    kp = torch.zeros(w.page_shape(4), dtype=torch.uint8, device=dev)
+    vp = torch.zeros(w.page_shape(4), dtype=torch.uint8, device=dev)
+    kraw = torch.from_numpy(w.rows("k")).to(dev)
+    vraw = torch.from_numpy(w.rows("v")).to(dev)
+    api.write_kv_pair(ctx, kraw, vraw, kp, vp, torch.from_numpy(w.slots).to(dev), 4, 4)
+    # the new rows: every non-empty sequence's last token (zeros for an empty one)
+    has = torch.from_numpy(w.seq_lens > 0).to(dev)
+    last = torch.from_numpy(np.maximum(w.cu_seqlens[1:] - 1, 0).astype(np.int64)).to(dev)
+    k_new = torch.where(has[:, None, None], kraw[last], torch.zeros_like(kraw[last])).contiguous()
+    v_new = torch.where(has[:, None, None], vraw[last], torch.zeros_like(vraw[last])).contiguous()
+    q = torch.from_numpy(w.queries()).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(api.decode_workspace_bytes(ctx, w.batch, w.num_q_heads, hkv, w.max_seq_len), dtype=torch.uint8,
+                     device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step():
+        api.paged_decode_append(ctx, q, k_new, v_new, kp, vp, bt, lens, 4, 4, max_seq_len=w.max_seq_len, out=out,
+                                workspace=ws, err_count=err, check_pages=False)
+
+    step()
+    torch.cuda.synchronize()
+    eager, kp_eager, vp_eager = out.clone(), kp.clone(), vp.clone()
+    assert int(err.item()) == 0
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))  # eager work between replays
+        junk = torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r} differs from the eager call"
+        assert torch.equal(kp, kp_eager) and torch.equal(vp, vp_eager), f"replay {r}: pages differ"
         del junk
     assert int(err.item()) == 0
