@@ -91,6 +91,16 @@ def test_status_strings_and_argument_errors():
     assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, p, p, 1, 16, p, 0.0, p, p, need - 4, None) == 4
     assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 16, p, 4, p, 64, p, p, 1, -1, p, 0.0, p, p, need, None) == 1  # cap < 0
     assert hy(h, p, 1, 2, 8, 2, p, 4, p, 4, 8, 32, p, 4, p, 64, p, p, 1, 16, p, 0.0, p, p, need, None) == 2  # block 32
+    # the one-call decode step: its own checks, then the decode's
+    ap = lib.tq_paged_decode_append
+    dneed = lib.tq_decode_workspace_bytes(h, 2, 8, 2, 64, 16)
+    assert ap(h, p, 1, 2, 8, 2, p, p, 7, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, dneed, None, None) == 1  # row dtype
+    assert ap(h, p, 1, 2, 8, 2, None, p, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, dneed, None, None) == 1  # no k_new
+    assert ap(h, p, 1, 2, 8, 2, p, ctypes.c_void_p(18), 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, dneed, None,
+              None) == 3  # v_new misaligned
+    assert ap(h, p, 1, 2, 8, 2, p, p, 1, p, 6, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, dneed, None, None) == 2  # K bits 6
+    assert ap(h, p, 1, 2, 8, 2, p, p, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, dneed - 4, None, None) == 4
+    assert ap(h, p, 1, 0, 8, 2, None, None, 1, p, 4, p, 4, 8, 16, p, 4, p, 64, 0.0, p, p, dneed, None, None) == 0
     # the prod key codec
     assert [lib.tq_prod_row_bytes(128, b) for b in (2, 3, 4, 5)] == [40, 56, 72, 88]
     assert lib.tq_prod_row_bytes(128, 1) == 0 and lib.tq_prod_row_bytes(100, 4) == 0
