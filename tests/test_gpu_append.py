@@ -13,7 +13,8 @@ the decode tolerance (2e-3 max-abs, 1e-3 rel-L2).  The cases cover:
 * new rows in fp32, fp16 and bf16;
 * sequences that end on a page's last row and on a page's first row, and an
   empty sequence;
-* a last page whose block id lies outside the pages (counted, not written).
+* a last page whose block id lies outside the pages (counted, not written);
+* the full long-context workload against the two-call path.
 """
 
 import numpy as np
@@ -140,3 +141,36 @@ def test_append_raises_when_checked(ctx):
     with pytest.raises(api.TQError):
         api.paged_decode_append(ctx, torch.from_numpy(w.queries()).cuda(), new, new, kp, vp,
                                 torch.from_numpy(bt).cuda(), torch.from_numpy(w.seq_lens).cuda(), 4, 4)
+
+
+def test_append_full_size_long_context(ctx):
+    # the long-context workload at full size (8 x 131072 tokens, 8 KV heads):
+    # every row but the last tokens' written by the GPU writer, then the step
+    # as one call and as two calls on copies of the pages; the pools and the
+    # outputs must be equal bit for bit (the oracle side of this path is
+    # covered at reduced size above and by the full-size decode tests)
+    w = workloads.preset("long_context")
+    print(f"[append] full size long_context: {w.num_tokens} tokens x {w.num_kv_heads} heads", flush=True)
+    assert api.decode_kernel(w.batch, w.num_q_heads, w.num_kv_heads, w.max_seq_len, 4, 4) == "staged"
+    dev = torch.device("cuda")
+    kraw = torch.from_numpy(w.rows("k", threads=16)).to(dev)
+    vraw = torch.from_numpy(w.rows("v", threads=16)).to(dev)
+    last = torch.from_numpy((w.cu_seqlens[1:] - 1).astype(np.int64)).to(dev)
+    slots = torch.from_numpy(w.slots).to(dev)
+    hist = slots.clone()
+    hist[last] = -1
+    kp1 = torch.zeros(w.page_shape(4), dtype=torch.uint8, device=dev)
+    vp1 = torch.zeros(w.page_shape(4), dtype=torch.uint8, device=dev)
+    api.write_kv_pair(ctx, kraw, vraw, kp1, vp1, hist, 4, 4)
+    k_new, v_new = kraw[last].contiguous(), vraw[last].contiguous()
+    del kraw, vraw
+    kp2, vp2 = kp1.clone(), vp1.clone()
+    q = torch.from_numpy(w.queries()).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    api.write_kv_pair(ctx, k_new, v_new, kp1, vp1, slots[last].contiguous(), 4, 4)
+    out1 = api.paged_decode(ctx, q, kp1, vp1, bt, lens, 4, 4, max_seq_len=w.max_seq_len)
+    out2 = api.paged_decode_append(ctx, q, k_new, v_new, kp2, vp2, bt, lens, 4, 4, max_seq_len=w.max_seq_len)
+    torch.cuda.synchronize()
+    assert torch.equal(kp1, kp2) and torch.equal(vp1, vp2), "pages differ from the two-call path"
+    assert torch.equal(out1, out2), "output differs from the two-call path"
