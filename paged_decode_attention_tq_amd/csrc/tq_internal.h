@@ -62,6 +62,8 @@ struct ProdScoreArgs {
   int32_t chunk_pages;           // pages per workgroup (a multiple of 4)
   int32_t chunks;                // ceil(pages of max_seq_len / chunk_pages)
   int32_t vec_store;             // scores rows 16-byte aligned (max_seq_len % 4 == 0, aligned base)
+  int32_t head_group;            // H: KV heads of one workgroup (a divisor of num_kv_heads)
+  int32_t phases;                // P = 4 / H: the waves of one head split its pages P ways
   uint32_t sign_bits[kHeadDim / 32];
   float cent[16];                // the 2^(bits-1) centroids of the index codebook, times 16
 };

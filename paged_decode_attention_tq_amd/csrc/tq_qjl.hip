@@ -93,12 +93,15 @@ __global__ __launch_bounds__(256) void prod_query_kernel(ProdScoreArgs a) {
 // supplies those coordinates' A and B values.  The result sits in lane
 // (n, c) as tokens 4 c .. 4 c + 3 of column n.
 //
-// Grid: one workgroup per (slab = sequence and chunk of pages, KV head,
-// chunk of 8 query heads), ordered so that all workgroups of a slab have
-// blockIdx congruent mod 8, i.e. run on one XCD and share its L2 for the
-// page lines that hold several KV heads' rows.  Each wave takes every
-// fourth page of the chunk, in batches of four pages whose row fields are
-// loaded while the previous batch is computed.
+// Grid: one workgroup of 4 waves per (slab = sequence and chunk of pages,
+// group of H KV heads, chunk of 8 query heads).  Wave w takes KV head w % H
+// of the group and every P-th page of the chunk from page w / H (P = 4 / H
+// phases), so with H > 1 the waves read the neighbouring rows of a page's KV
+// heads together and use whole cache lines; with H = 1 each wave takes every
+// fourth page of one head.  Workgroups of one slab have blockIdx congruent
+// mod 8, i.e. run on one XCD and share its L2 for the page lines that hold
+// several KV heads' rows.  A wave walks its pages in batches of four whose
+// row fields are loaded while the previous batch is computed.
 
 constexpr float kCentScale = 16.0f;  // the host passes centroids times 16 (exact)
 
@@ -132,11 +135,16 @@ __global__ __launch_bounds__(256) void prod_scores_kernel(ProdScoreArgs a) {
   const int n = lane & 15, c = lane >> 4;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int nhc = (G + 7) / 8;
-  const int inner = a.num_kv_heads * nhc;
+  const int ngroups = a.num_kv_heads / a.head_group;
+  const int inner = ngroups * nhc;
   const int r8 = (int)(blockIdx.x >> 3);
   const int64_t slab = (int64_t)(r8 / inner) * 8 + (blockIdx.x & 7);
   if (slab >= (int64_t)a.batch * a.chunks) return;  // uniform per workgroup
-  const int g = (r8 % inner) % a.num_kv_heads, hc = (r8 % inner) / a.num_kv_heads;
+  const int hc = (r8 % inner) / ngroups;
+  // wave: KV head g of the workgroup's group, page phase ph (pages ph, ph + P, ...)
+  const int ph = wave / a.head_group;
+  const bool active = ph < a.phases;
+  const int g = ((r8 % inner) % ngroups) * a.head_group + wave % a.head_group;
   const int b = (int)(slab / a.chunks), ck = (int)(slab % a.chunks);
 
   const int L = min(max(a.seq_lens[b], 0), a.max_len);
@@ -201,6 +209,7 @@ __global__ __launch_bounds__(256) void prod_scores_kernel(ProdScoreArgs a) {
   for (int m = 0; m < 4; ++m) Bs[m] = __builtin_bit_cast(half8, u32x4{bs[4 * m], bs[4 * m + 1], bs[4 * m + 2], bs[4 * m + 3]});
   const float zq = inv_s * 0.009791516697777346f;  // sqrt(pi / 2) / 128 over the S q~ scale
   __syncthreads();
+  if (!active) return;  // uniform per wave; no barrier follows
 
   const uint32_t lane_off = 8u * (uint32_t)(lane & 31);
   // scores of the chunk's heads through one buffer descriptor (the host
@@ -297,25 +306,26 @@ __global__ __launch_bounds__(256) void prod_scores_kernel(ProdScoreArgs a) {
                                               0, 0);
     }
   };
-  // pages pg, pg + 4, ... of this wave in batches of four, two batch
+  // pages pg, pg + P, ... of this wave in batches of four, two batch
   // buffers in turn: a batch's rows are requested while the previous batch
   // is computed
+  const int P = a.phases;
   Rows da[4], db[4];
-  const int pg0 = pg_first + wave;
+  const int pg0 = pg_first + ph;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) fetch(pg0 + 4 * u, da[u]);
-  for (int pg = pg0; pg < pg_end; pg += 32) {
+  for (int u = 0; u < 4; ++u) fetch(pg0 + P * u, da[u]);
+  for (int pg = pg0; pg < pg_end; pg += 8 * P) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) fetch(pg + 16 + 4 * u, db[u]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (pg + 4 * u < pg_end) tile(pg + 4 * u, da[u]);  // uniform per wave
-    if (pg + 16 >= pg_end) break;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) fetch(pg + 32 + 4 * u, da[u]);
+    for (int u = 0; u < 4; ++u) fetch(pg + P * (4 + u), db[u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (pg + 16 + 4 * u < pg_end) tile(pg + 16 + 4 * u, db[u]);
+      if (pg + P * u < pg_end) tile(pg + P * u, da[u]);  // uniform per wave
+    if (pg + 4 * P >= pg_end) break;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fetch(pg + P * (8 + u), da[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (pg + P * (4 + u) < pg_end) tile(pg + P * (4 + u), db[u]);
   }
 }
 
@@ -326,10 +336,10 @@ hipError_t launch_prod_scores(const ProdScoreArgs& a, int bits, hipStream_t stre
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_seq_len == 0) return e;
   const int G = a.num_q_heads / a.num_kv_heads, nhc = (G + 7) / 8;
-  const int64_t inner = (int64_t)a.num_kv_heads * nhc;
+  const int64_t inner = (int64_t)(a.num_kv_heads / a.head_group) * nhc;
   const int64_t slabs = (int64_t)a.batch * a.chunks;
   const int64_t wgs = (slabs + 7) / 8 * 8 * inner;
-  if (wgs > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (wgs > 0x7fffffffLL || a.head_group * a.phases > 4 || a.num_kv_heads % a.head_group) return hipErrorInvalidValue;
   const dim3 grid((unsigned)wgs), block(256);
   switch (bits) {
     case 2: hipLaunchKernelGGL(prod_scores_kernel<2>, grid, block, 0, stream, a); break;

@@ -83,10 +83,12 @@ def test_writer_matches_oracle(ctx, bits, dt):
 
 # lengths past 512 tokens span several 32-page chunks of the score kernel;
 # groups above 8 split a KV head's query heads over workgroups (12: a short tail);
-# 601 columns take the scalar score stores
+# 601 columns take the scalar score stores; 8 and 16 KV heads put four
+# neighbouring heads in one workgroup (one per wave)
 @pytest.mark.parametrize("bits,hkv,G,lens", [(4, 2, 8, [200, 17, 0, 64]), (3, 1, 4, [200, 17, 0, 64]),
                                              (2, 4, 2, [200, 17, 0, 64]), (5, 2, 3, [200, 17, 0, 64]),
-                                             (4, 1, 12, [1100, 17, 0, 530]), (3, 2, 16, [601, 513, 1])])
+                                             (4, 1, 12, [1100, 17, 0, 530]), (3, 2, 16, [601, 513, 1]),
+                                             (4, 8, 8, [1100, 17, 0, 530]), (3, 16, 2, [601, 45, 1])])
 def test_scores_match_oracle(ctx, bits, hkv, G, lens):
     w = workloads.make_workload(f"qjls{bits}", num_q_heads=hkv * G, num_kv_heads=hkv, seq_lens=lens,
                                 seed=120 + bits, outlier_frac=0.02)
